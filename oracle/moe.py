@@ -1,0 +1,174 @@
+"""Plain fp64 evaluation of one DeepSeekMoE layer (test infrastructure only).
+
+Sources (titles and sections of the pages the method is taken from):
+  [P1] "DeepSeekMoE" translated paper page: section 2 eq. 3-5 (top-K MoE
+       layer), section 3.1 eq. 6-8 (fine-grained experts), section 3.2
+       eq. 9-11 (shared experts, routed top-(mK-K_s) gates).
+  [P4] MoE-survey blog page ("six MoE papers"): section 2 (sparsely-gated
+       MoE: y = sum_i G(x)_i E_i(x), experts with zero gate are skipped;
+       noisy top-k gating G = Softmax(KeepTopK(H, k))), section 4 (Switch
+       routing: p = softmax over all N experts, y = sum over the top-k of
+       p_i E_i(x)), section 5 (router probabilities kept in float32).
+
+Everything is float64.  Inputs are the exact values the GPU consumes (bf16
+bit patterns or float32 decoded losslessly), so the only difference between
+this and the GPU is rounding inside the computation.
+
+Readings taken where the pages leave a step open:
+  * softmax runs over the N_r routed experts only; shared experts have no
+    centroid (eq. 10-11 index the gates from K_s+1).
+  * "softmax_topk" gates are s_i on the chosen experts, not renormalised
+    (eq. 10); "topk_softmax" is Softmax(KeepTopK(z, K')) with no noise.
+  * expert FFN is the SiLU-gated form W2 (silu(W1 u) * (W3 u)).
+  * top-k ties break toward the lower expert id; chosen ids are reported
+    in ascending order.
+  * shared experts enter with weight 1 (eq. 9, first sum); the residual
+    u_t of eq. 9 is added only when asked for.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GATES = ("softmax_topk", "topk_softmax")
+
+
+def decode(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Storage array -> float64.  bf16 arrive as uint16 bit patterns."""
+    if a is None:
+        return None
+    if dtype == "bf16" and a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return np.asarray(a, dtype=np.float64)
+
+
+def router_logits(x: np.ndarray, w_router: np.ndarray, bias=None) -> np.ndarray:
+    """Token-to-centroid affinities u_t^T e_i for every routed expert ([P1] eq. 5/11),
+    plus an optional per-expert bias.  x [T, d], w_router [N_r, d] (row i = e_i)."""
+    z = x @ w_router.T
+    if bias is not None:
+        z = z + bias[None, :]
+    return z
+
+
+def softmax(z: np.ndarray) -> np.ndarray:
+    """Row-wise softmax over the last axis."""
+    m = np.max(z, axis=-1, keepdims=True)
+    e = np.exp(z - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def select_topk(score: np.ndarray, k: int) -> np.ndarray:
+    """Ids of the k largest scores per row, ties to the lower id, ascending ids.
+
+    Topk(., K) of [P1] eq. 4/7/10 and KeepTopK of [P4] section 2."""
+    order = np.argsort(-score, axis=1, kind="stable")[:, :k]
+    return np.sort(order, axis=1)
+
+
+def gate_values(z: np.ndarray, idx: np.ndarray, gate: str) -> np.ndarray:
+    """Gate values g_{i,t} on the chosen experts idx [T, K'] from logits z [T, N_r]."""
+    if gate == "softmax_topk":
+        # g = s on the kept experts, s = Softmax over all routed experts ([P1] eq. 10-11).
+        s = softmax(z)
+        return np.take_along_axis(s, idx, axis=1)
+    if gate == "topk_softmax":
+        # KeepTopK sets the others to -inf, so the softmax runs over the kept set ([P4] sec. 2).
+        zk = np.take_along_axis(z, idx, axis=1)
+        return softmax(zk)
+    raise ValueError(f"unknown gate {gate!r}")
+
+
+def route(z: np.ndarray, k: int, gate: str):
+    """Selection + gate values.  Selection is on s for softmax_topk ([P1] eq. 10)
+    and on the logits for topk_softmax ([P4] KeepTopK); both orders agree."""
+    if gate == "softmax_topk":
+        idx = select_topk(softmax(z), k)
+    elif gate == "topk_softmax":
+        idx = select_topk(z, k)
+    else:
+        raise ValueError(f"unknown gate {gate!r}")
+    return idx.astype(np.int32), gate_values(z, idx, gate)
+
+
+def dispatch(idx: np.ndarray, n_routed: int):
+    """Per-expert token lists for evaluating only the chosen experts ([P4] sec. 2).
+
+    Returns counts [N_r], offsets [N_r+1] (exclusive scan), row_token [P]
+    (the token of each row; rows grouped by expert, tokens ascending within an
+    expert) and slot_row [P] (row of slot t*K'+j)."""
+    T, k = idx.shape
+    flat = idx.reshape(-1).astype(np.int64)
+    counts = np.bincount(flat, minlength=n_routed).astype(np.int32)
+    offsets = np.zeros(n_routed + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    order = np.argsort(flat, kind="stable")          # slot ids sorted by expert, then slot
+    row_token = (order // k).astype(np.int32)
+    slot_row = np.empty(T * k, dtype=np.int32)
+    slot_row[order] = np.arange(T * k, dtype=np.int32)
+    return counts, offsets, row_token, slot_row
+
+
+def silu(a: np.ndarray) -> np.ndarray:
+    return a / (1.0 + np.exp(-a))
+
+
+def expert_ffn(X: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray) -> np.ndarray:
+    """SiLU-gated FFN_i(u) = W2 (silu(W1 u) * (W3 u)) on the rows of X.
+    w_gate, w_up [I, d]; w_down [d, I]."""
+    return (silu(X @ w_gate.T) * (X @ w_up.T)) @ w_down.T
+
+
+def shared_ffn(X: np.ndarray, ws_gate, ws_up, ws_down) -> np.ndarray:
+    """Sum over the K_s shared experts, each with weight 1 ([P1] eq. 9, first sum)."""
+    y = np.zeros((X.shape[0], X.shape[1]), dtype=np.float64)
+    for s in range(ws_gate.shape[0]):
+        y += expert_ffn(X, ws_gate[s], ws_up[s], ws_down[s])
+    return y
+
+
+def forward(cfg, inputs: dict, tokens=None, residual: bool = False) -> dict:
+    """The layer forward ([P1] eq. 9-11) on storage-form inputs from synth.
+
+    tokens: optional array of token ids; y is then computed for those tokens
+    only (routing and dispatch are always for the whole batch).
+    """
+    dt = cfg.dtype
+    x = decode(inputs["x"], dt)
+    wr = np.asarray(inputs["w_router"], dtype=np.float64)
+    b = None if inputs.get("bias") is None else np.asarray(inputs["bias"], dtype=np.float64)
+    T, d = x.shape
+    Nr, k = cfg.n_routed, cfg.top_k
+
+    z = router_logits(x, wr, b)
+    idx, g = route(z, k, cfg.gate)
+    counts, offsets, row_token, slot_row = dispatch(idx, Nr)
+
+    sel = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    pos = np.full(T, -1, dtype=np.int64)
+    pos[sel] = np.arange(sel.size)
+    y = np.zeros((sel.size, d), dtype=np.float64)
+
+    # Routed experts, ascending expert id, each on the tokens that chose it.
+    for e in range(Nr):
+        rows = np.arange(offsets[e], offsets[e + 1])
+        toks = row_token[rows]
+        keep = pos[toks] >= 0
+        if not np.any(keep):
+            continue
+        toks = toks[keep]
+        slots = np.nonzero(idx[toks] == e)[1]
+        ge = g[toks, slots]
+        F = expert_ffn(x[toks], decode(inputs["w_gate"][e], dt),
+                       decode(inputs["w_up"][e], dt), decode(inputs["w_down"][e], dt))
+        y[pos[toks]] += ge[:, None] * F
+
+    if cfg.n_shared > 0:
+        y += shared_ffn(x[sel], decode(inputs["ws_gate"], dt),
+                        decode(inputs["ws_up"], dt), decode(inputs["ws_down"], dt))
+    if residual:
+        y += x[sel]
+
+    return {
+        "logits": z, "topk_idx": idx, "topk_w": g, "counts": counts, "offsets": offsets,
+        "row_token": row_token, "slot_row": slot_row, "tokens": sel, "y": y,
+    }

@@ -1,0 +1,77 @@
+"""Pure-Python brute force of the MoE layer for tiny shapes (pins the oracle).
+
+Written independently of oracle/: plain loops and the math module, no
+numpy, no dispatch.  Every routed expert is evaluated for every token and
+multiplied by its gate, which is zero for the experts not chosen; this is the
+dense form y = sum_i G(x)_i E_i(x) of the sparsely-gated MoE (MoE-survey blog
+page, section 2) and eq. 9 of the DeepSeekMoE page, section 3.2.
+"""
+from __future__ import annotations
+
+import math
+
+
+def _dot(a, b):
+    s = 0.0
+    for p, q in zip(a, b):
+        s += p * q
+    return s
+
+
+def _ffn(u, w1, w3, w2):
+    # w1, w3: I rows of length d; w2: d rows of length I
+    h = []
+    for r1, r3 in zip(w1, w3):
+        a = _dot(r1, u)
+        h.append(a * (1.0 / (1.0 + math.exp(-a))) * _dot(r3, u))
+    return [_dot(row, h) for row in w2]
+
+
+def _gates(z, k, gate):
+    n = len(z)
+    g = [0.0] * n
+    if gate == "softmax_topk":
+        m = max(z)
+        ex = [math.exp(v - m) for v in z]
+        tot = sum(ex)
+        s = [v / tot for v in ex]
+        chosen = sorted(range(n), key=lambda i: (-s[i], i))[:k]
+        for i in chosen:
+            g[i] = s[i]
+    elif gate == "topk_softmax":
+        chosen = sorted(range(n), key=lambda i: (-z[i], i))[:k]
+        m = max(z[i] for i in chosen)
+        tot = sum(math.exp(z[i] - m) for i in chosen)
+        for i in chosen:
+            g[i] = math.exp(z[i] - m) / tot
+    else:
+        raise ValueError(gate)
+    return sorted(chosen), g
+
+
+def brute_forward(x, w_router, bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
+                  top_k, gate, residual=False):
+    """All arguments are nested Python lists of floats (bias may be None).
+
+    Returns (chosen ids per token, ascending; dense gates per token; y)."""
+    chosen_all, g_all, y_all = [], [], []
+    n = len(w_router)
+    for u in x:
+        z = [_dot(w_router[i], u) + (bias[i] if bias is not None else 0.0) for i in range(n)]
+        chosen, g = _gates(z, top_k, gate)
+        y = [0.0] * len(u)
+        for i in range(n):                       # dense: every routed expert
+            f = _ffn(u, w_gate[i], w_up[i], w_down[i])
+            for c in range(len(u)):
+                y[c] += g[i] * f[c]
+        for s in range(len(ws_gate)):            # shared experts, gate 1
+            f = _ffn(u, ws_gate[s], ws_up[s], ws_down[s])
+            for c in range(len(u)):
+                y[c] += f[c]
+        if residual:
+            for c in range(len(u)):
+                y[c] += u[c]
+        chosen_all.append(chosen)
+        g_all.append(g)
+        y_all.append(y)
+    return chosen_all, g_all, y_all
