@@ -1,0 +1,155 @@
+/*
+ * moe.h -- C ABI of libmoe.so: forward pass of one DeepSeekMoE layer on a
+ * gfx950 (MI355X) GPU.
+ *
+ * The layer (DeepSeekMoE paper page, section 3.2, eq. 9-11):
+ *   z_t   = W_g u_t (+ b)                      router logits, fp32
+ *   S_t   = top-K' routed experts of token t
+ *   g     = s on S_t, s = Softmax over the N_r routed experts       (eq. 10-11)
+ *        or Softmax over S_t of z (KeepTopK, noise 0; MoE-survey blog page,
+ *           section 2, noisy top-k gating)
+ *   y_t   = sum_{i in S_t} g_i FFN_i(u_t) + sum_{s < K_s} FFN^sh_s(u_t) (+ u_t)
+ *   FFN(u)= W2 (silu(W1 u) * (W3 u))
+ * Only the chosen experts are evaluated (MoE-survey blog page, section 2:
+ * E_i is skipped where G(x)_i = 0), which is why the work is split into
+ * route -> permute (dispatch) -> expert FFN -> combine.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are dense and row-major.  Every data pointer is a device
+ *     pointer owned by the caller; the library never allocates, frees or
+ *     synchronises, and holds no global state besides the thread-local last
+ *     HIP error.  Scratch memory comes only from the caller's `ws` buffer,
+ *     sized by moe_workspace_size().
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call only enqueues work on it and returns.
+ *   - Weights are [out_features, in_features] (in_features contiguous):
+ *       w_router [N_r, d] fp32 (row i is the centroid e_i),
+ *       w_gate, w_up [N_r, I, d], w_down [N_r, d, I],
+ *       ws_gate, ws_up [K_s, I_s, d], ws_down [K_s, d, I_s].
+ *     x, y, expert weights and intermediate buffers use layer->dtype
+ *     (MOE_BF16: bfloat16 with fp32 accumulation; MOE_F32: float32).
+ *   - Routing outputs: topk_idx [T, K'] int32 ascending within a token,
+ *     topk_w [T, K'] fp32 aligned with it.  Rows of expert e occupy
+ *     [offsets[e], offsets[e+1]) in ascending token order.  P = T*K'.
+ *   - Errors: every argument check runs on the host before anything is
+ *     enqueued; on failure nothing is launched.  A failed launch returns
+ *     MOE_ERR_HIP and moe_last_hip_error() gives the hipError_t.  Faults
+ *     inside kernels surface at the caller's next synchronisation.
+ *   - Requirements (else MOE_ERR_UNSUPPORTED): N_r <= 256, 1 <= K' <= 16,
+ *     K' <= N_r; for MOE_BF16, d % 64 == 0, I % 64 == 0, I_s % 64 == 0;
+ *     for MOE_F32, d % 4 == 0, I % 4 == 0, I_s % 4 == 0; T < 2^31 / 16;
+ *     all pointers 16-byte aligned.  T == 0 returns MOE_OK with no work.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,          /* null required pointer, T < 0, bad enum, K' out of range */
+  MOE_ERR_UNSUPPORTED = 2,          /* shape/alignment outside the supported set above         */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,  /* ws_bytes below moe_workspace_size()                      */
+  MOE_ERR_HIP = 4                   /* a HIP launch or query failed                              */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum {
+  /* g_i = s_i on the top-K' of s = Softmax over N_r routed experts, not
+     renormalised (DeepSeekMoE page, section 3.2, eq. 10-11).            */
+  MOE_GATE_SOFTMAX_TOPK = 0,
+  /* g = Softmax(KeepTopK(z, K')) with zero noise (MoE-survey blog page,
+     section 2, noisy top-k gating).                                      */
+  MOE_GATE_TOPK_SOFTMAX = 1
+} moe_gate;
+
+/* Shape of one layer.  n_routed = N_r = mN - K_s, top_k = K' = mK - K_s. */
+typedef struct {
+  int32_t d_model;      /* d                                  */
+  int32_t n_routed;     /* N_r                                */
+  int32_t n_shared;     /* K_s (0 allowed)                    */
+  int32_t top_k;        /* K'                                 */
+  int32_t d_ff;         /* I, width of one routed expert      */
+  int32_t d_ff_shared;  /* I_s, width of one shared expert    */
+  int32_t gate;         /* moe_gate                           */
+  int32_t dtype;        /* moe_dtype                          */
+} moe_layer;
+
+int moe_abi_version(void);
+const char* moe_status_str(int status);
+/* hipError_t of the last failed HIP call made by this thread (0 if none). */
+int moe_last_hip_error(void);
+
+/* Bytes of scratch that every entry point below needs for T tokens (host
+ * only, no GPU call).  One buffer of this size serves all of them. */
+int moe_workspace_size(const moe_layer* layer, int64_t T, size_t* bytes);
+
+/* Router: logits z = x W_g^T (+ logit_bias) in fp32, gate values and the
+ * top-K' choice per token (eq. 10-11; KeepTopK variant per layer->gate).
+ * Ties between equal logits go to the lower expert id.
+ *   x [T, d] (dtype), w_router [N_r, d] fp32, logit_bias [N_r] fp32 or NULL
+ *   (added to the logits before both selection and softmax)
+ *   -> topk_idx [T, K'] int32 (ascending), topk_w [T, K'] fp32. */
+int moe_route(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
+              const float* logit_bias, int32_t* topk_idx, float* topk_w, void* stream);
+
+/* Dispatch: stable counting sort of the T*K' (token, expert) assignments by
+ * expert (the per-expert token lists that let only chosen experts run).
+ *   topk_idx [T, K'] with 0 <= id < N_r and distinct ids per token (other
+ *   input is undefined behaviour), x [T, d] (dtype)
+ *   -> counts [N_r], offsets [N_r + 1] (exclusive scan, offsets[N_r] = P),
+ *      row_token [P] (token of each row), slot_row [P] (row of slot t*K'+j),
+ *      x_perm [P, d] (x_perm[r] = x[row_token[r]]; NULL skips the copy). */
+int moe_permute(const moe_layer* layer, int64_t T, const int32_t* topk_idx, const void* x,
+                int32_t* counts, int32_t* offsets, int32_t* row_token, int32_t* slot_row,
+                void* x_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* Routed experts: for every expert e and row r in [offsets[e], offsets[e+1]):
+ *   y_perm[r] = W2_e (silu(W1_e x_perm[r]) * (W3_e x_perm[r]))
+ * (FFN_i of eq. 9, unweighted; the gate is applied by moe_combine).
+ * Intermediate activations are rounded to dtype.  Reads offsets on the
+ * device (no host synchronisation).  y_perm [P, d]. */
+int moe_expert_ffn(const moe_layer* layer, int64_t T, const int32_t* offsets, const void* x_perm,
+                   const void* w_gate, const void* w_up, const void* w_down, void* y_perm,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* Shared experts (eq. 9, first sum, gate 1), evaluated as one FFN of width
+ * K_s*I_s: y_shared[t] = sum_s FFN^sh_s(x[t]).  y_shared [T, d].
+ * With K_s == 0 it writes zeros. */
+int moe_shared_ffn(const moe_layer* layer, int64_t T, const void* x, const void* ws_gate,
+                   const void* ws_up, const void* ws_down, void* y_shared, void* ws,
+                   size_t ws_bytes, void* stream);
+
+/* Gate-weighted combine (eq. 9):
+ *   y[t] = sum_j topk_w[t,j] * y_perm[slot_row[t*K'+j]] + y_shared[t] + residual[t]
+ * in fp32, j ascending, one rounding to dtype.  y_shared and residual may be
+ * NULL (then omitted).  y [T, d]. */
+int moe_combine(const moe_layer* layer, int64_t T, const void* y_perm, const int32_t* slot_row,
+                const float* topk_w, const void* y_shared, const void* residual, void* y,
+                void* stream);
+
+/* The whole layer: route, dispatch, routed and shared experts, combine.
+ * The gather of x rows is fused into the routed gate/up GEMM, so no x_perm
+ * is materialised.  residual (NULL or [T, d], usually x itself) is added
+ * last.  topk_idx, topk_w, counts and offsets are written for inspection
+ * and may be NULL (then they live in ws).  y [T, d]. */
+int moe_forward(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
+                const float* logit_bias, const void* w_gate, const void* w_up,
+                const void* w_down, const void* ws_gate, const void* ws_up,
+                const void* ws_down, const void* residual, void* y, int32_t* topk_idx,
+                float* topk_w, int32_t* counts, int32_t* offsets, void* ws, size_t ws_bytes,
+                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,404 @@
+// C ABI of libmoe (declared in include/moe.h): argument checks, workspace
+// carving and the launch sequence of each entry point.  Every check runs on
+// the host before anything is enqueued.
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  size_t block_counts, block_base, local_rank, topk_idx, topk_w, counts, offsets, row_token,
+      slot_row, h, y_perm, h_shared, y_shared, total;
+};
+
+size_t elt_bytes(const moe_layer* L) { return L->dtype == MOE_BF16 ? 2 : 4; }
+
+Layout layout_of(const moe_layer* L, int64_t T) {
+  Layout o{};
+  const size_t P = static_cast<size_t>(T) * L->top_k;
+  const size_t NB = static_cast<size_t>((T + moe::kCountBlock - 1) / moe::kCountBlock);
+  const size_t Nr = L->n_routed, e = elt_bytes(L), d = L->d_model;
+  size_t cur = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = cur;
+    cur += align_up(bytes);
+    return at;
+  };
+  o.block_counts = take(NB * Nr * 4);
+  o.block_base = take(NB * Nr * 4);
+  o.local_rank = take(P * 4);
+  o.topk_idx = take(P * 4);
+  o.topk_w = take(P * 4);
+  o.counts = take(Nr * 4);
+  o.offsets = take((Nr + 1) * 4);
+  o.row_token = take(P * 4);
+  o.slot_row = take(P * 4);
+  o.h = take(P * L->d_ff * e);
+  o.y_perm = take(P * d * e);
+  const size_t wsh = static_cast<size_t>(L->n_shared) * (L->n_shared > 0 ? L->d_ff_shared : 0);
+  o.h_shared = take(static_cast<size_t>(T) * wsh * e);
+  o.y_shared = take(L->n_shared > 0 ? static_cast<size_t>(T) * d * e : 0);
+  o.total = cur;
+  return o;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_layer(const moe_layer* L, int64_t T) {
+  if (L == nullptr || T < 0) return MOE_ERR_INVALID_ARG;
+  if (L->dtype != MOE_F32 && L->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (L->gate != MOE_GATE_SOFTMAX_TOPK && L->gate != MOE_GATE_TOPK_SOFTMAX) return MOE_ERR_INVALID_ARG;
+  if (L->d_model <= 0 || L->n_routed <= 0 || L->n_shared < 0 || L->d_ff <= 0)
+    return MOE_ERR_INVALID_ARG;
+  if (L->n_shared > 0 && L->d_ff_shared <= 0) return MOE_ERR_INVALID_ARG;
+  if (L->top_k < 1 || L->top_k > L->n_routed || L->top_k > 16) return MOE_ERR_INVALID_ARG;
+  if (L->n_routed > 256) return MOE_ERR_UNSUPPORTED;
+  if (T >= (int64_t{1} << 31) / 16) return MOE_ERR_UNSUPPORTED;
+  const int q = (L->dtype == MOE_BF16) ? 64 : 4;
+  if (L->d_model % q != 0 || L->d_ff % q != 0) return MOE_ERR_UNSUPPORTED;
+  if (L->n_shared > 0 && L->d_ff_shared % q != 0) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// Required pointer: non-null and 16-byte aligned.
+int need(const void* p) {
+  if (p == nullptr) return MOE_ERR_INVALID_ARG;
+  return aligned16(p) ? MOE_OK : MOE_ERR_UNSUPPORTED;
+}
+// Pointer to a buffer with T rows: required unless T == 0.
+int needT(const void* p, int64_t T) { return T == 0 ? (p == nullptr || aligned16(p) ? MOE_OK : MOE_ERR_UNSUPPORTED) : need(p); }
+// Optional pointer: null, or 16-byte aligned.
+int opt(const void* p) { return (p == nullptr || aligned16(p)) ? MOE_OK : MOE_ERR_UNSUPPORTED; }
+
+#define MOE_TRY(expr)             \
+  do {                            \
+    const int _st = (expr);       \
+    if (_st != MOE_OK) return _st; \
+  } while (0)
+
+#define MOE_HIP(expr)                          \
+  do {                                         \
+    const hipError_t _e = (expr);              \
+    if (_e != hipSuccess) {                    \
+      g_last_hip_error = static_cast<int>(_e); \
+      return MOE_ERR_HIP;                      \
+    }                                          \
+  } while (0)
+
+char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+moe::GemmArgs routed_gate_up(const moe_layer* L, int64_t T, const int32_t* offsets,
+                             const void* A, const int32_t* gather, const void* w_gate,
+                             const void* w_up, void* H) {
+  moe::GemmArgs g{};
+  g.offsets = offsets;
+  g.n_groups = L->n_routed;
+  g.rows_total = T * L->top_k;
+  g.A = A;
+  g.lda = L->d_model;
+  g.gather = gather;
+  g.B0 = w_gate;
+  g.B1 = w_up;
+  g.ldb = L->d_model;
+  g.b_group_stride = static_cast<int64_t>(L->d_ff) * L->d_model;
+  g.k_sub = L->d_model;
+  g.b_sub_stride = 0;
+  g.N = L->d_ff;
+  g.K = L->d_model;
+  g.C = H;
+  g.ldc = L->d_ff;
+  g.mode = moe::kGateUp;
+  return g;
+}
+
+moe::GemmArgs routed_down(const moe_layer* L, int64_t T, const int32_t* offsets, const void* H,
+                          const void* w_down, void* y_perm) {
+  moe::GemmArgs g{};
+  g.offsets = offsets;
+  g.n_groups = L->n_routed;
+  g.rows_total = T * L->top_k;
+  g.A = H;
+  g.lda = L->d_ff;
+  g.gather = nullptr;
+  g.B0 = w_down;
+  g.B1 = nullptr;
+  g.ldb = L->d_ff;
+  g.b_group_stride = static_cast<int64_t>(L->d_model) * L->d_ff;
+  g.k_sub = L->d_ff;
+  g.b_sub_stride = 0;
+  g.N = L->d_model;
+  g.K = L->d_ff;
+  g.C = y_perm;
+  g.ldc = L->d_model;
+  g.mode = moe::kDown;
+  return g;
+}
+
+int gemm(const moe_layer* L, const moe::GemmArgs& g, hipStream_t s) {
+  MOE_HIP(L->dtype == MOE_BF16 ? moe::launch_gemm_bf16(g, s) : moe::launch_gemm_f32(g, s));
+  return MOE_OK;
+}
+
+int run_shared(const moe_layer* L, int64_t T, const void* x, const void* ws_gate,
+               const void* ws_up, const void* ws_down, void* y_shared, void* h_shared,
+               hipStream_t s) {
+  const int wsh = L->n_shared * L->d_ff_shared;
+  moe::GemmArgs g{};
+  g.offsets = nullptr;
+  g.n_groups = 1;
+  g.rows_total = T;
+  g.A = x;
+  g.lda = L->d_model;
+  g.B0 = ws_gate;  // [K_s, I_s, d] is [K_s*I_s, d]: one FFN of width K_s*I_s
+  g.B1 = ws_up;
+  g.ldb = L->d_model;
+  g.k_sub = L->d_model;
+  g.N = wsh;
+  g.K = L->d_model;
+  g.C = h_shared;
+  g.ldc = wsh;
+  g.mode = moe::kGateUp;
+  MOE_TRY(gemm(L, g, s));
+  moe::GemmArgs h{};
+  h.offsets = nullptr;
+  h.n_groups = 1;
+  h.rows_total = T;
+  h.A = h_shared;
+  h.lda = wsh;
+  h.B0 = ws_down;  // K runs over the K_s matrices [d, I_s] in turn
+  h.ldb = L->d_ff_shared;
+  h.k_sub = L->d_ff_shared;
+  h.b_sub_stride = static_cast<int64_t>(L->d_model) * L->d_ff_shared;
+  h.N = L->d_model;
+  h.K = wsh;
+  h.C = y_shared;
+  h.ldc = L->d_model;
+  h.mode = moe::kDown;
+  return gemm(L, h, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape, dtype or alignment";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+int moe_last_hip_error(void) { return g_last_hip_error; }
+
+int moe_workspace_size(const moe_layer* layer, int64_t T, size_t* bytes) {
+  MOE_TRY(check_layer(layer, T));
+  if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
+  *bytes = layout_of(layer, T).total;
+  return MOE_OK;
+}
+
+int moe_route(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
+              const float* logit_bias, int32_t* topk_idx, float* topk_w, void* stream) {
+  MOE_TRY(check_layer(layer, T));
+  MOE_TRY(needT(x, T));
+  MOE_TRY(need(w_router));
+  MOE_TRY(opt(logit_bias));
+  MOE_TRY(needT(topk_idx, T));
+  MOE_TRY(needT(topk_w, T));
+  if (T == 0) return MOE_OK;
+  moe::RouteArgs a{};
+  a.x = x;
+  a.w_router = w_router;
+  a.bias = logit_bias;
+  a.T = static_cast<int>(T);
+  a.d = layer->d_model;
+  a.n_routed = layer->n_routed;
+  a.top_k = layer->top_k;
+  a.gate = layer->gate;
+  a.x_bf16 = layer->dtype == MOE_BF16;
+  a.topk_idx = topk_idx;
+  a.topk_w = topk_w;
+  MOE_HIP(moe::launch_route(a, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+static int permute_impl(const moe_layer* layer, int64_t T, const int32_t* topk_idx,
+                        const void* x, int32_t* counts, int32_t* offsets, int32_t* row_token,
+                        int32_t* slot_row, void* x_perm, void* ws, const Layout& lo,
+                        hipStream_t s) {
+  moe::PermuteArgs a{};
+  a.topk_idx = topk_idx;
+  a.x = x;
+  a.T = static_cast<int>(T);
+  a.d = layer->d_model;
+  a.n_routed = layer->n_routed;
+  a.top_k = layer->top_k;
+  a.elt_bytes = static_cast<int>(elt_bytes(layer));
+  a.counts = counts;
+  a.offsets = offsets;
+  a.row_token = row_token;
+  a.slot_row = slot_row;
+  a.x_perm = x_perm;
+  a.block_counts = reinterpret_cast<int32_t*>(at(ws, lo.block_counts));
+  a.block_base = reinterpret_cast<int32_t*>(at(ws, lo.block_base));
+  a.local_rank = reinterpret_cast<int32_t*>(at(ws, lo.local_rank));
+  MOE_HIP(moe::launch_permute(a, s));
+  return MOE_OK;
+}
+
+int moe_permute(const moe_layer* layer, int64_t T, const int32_t* topk_idx, const void* x,
+                int32_t* counts, int32_t* offsets, int32_t* row_token, int32_t* slot_row,
+                void* x_perm, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_layer(layer, T));
+  MOE_TRY(needT(topk_idx, T));
+  MOE_TRY(need(counts));
+  MOE_TRY(need(offsets));
+  MOE_TRY(needT(row_token, T));
+  MOE_TRY(needT(slot_row, T));
+  MOE_TRY(opt(x_perm));
+  if (x_perm != nullptr) MOE_TRY(needT(x, T));
+  MOE_TRY(need(ws));
+  const Layout lo = layout_of(layer, T);
+  if (ws_bytes < lo.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return permute_impl(layer, T, topk_idx, x, counts, offsets, row_token, slot_row, x_perm, ws,
+                      lo, static_cast<hipStream_t>(stream));
+}
+
+int moe_expert_ffn(const moe_layer* layer, int64_t T, const int32_t* offsets, const void* x_perm,
+                   const void* w_gate, const void* w_up, const void* w_down, void* y_perm,
+                   void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_layer(layer, T));
+  MOE_TRY(need(offsets));
+  MOE_TRY(needT(x_perm, T));
+  MOE_TRY(need(w_gate));
+  MOE_TRY(need(w_up));
+  MOE_TRY(need(w_down));
+  MOE_TRY(needT(y_perm, T));
+  MOE_TRY(need(ws));
+  const Layout lo = layout_of(layer, T);
+  if (ws_bytes < lo.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* H = at(ws, lo.h);
+  MOE_TRY(gemm(layer, routed_gate_up(layer, T, offsets, x_perm, nullptr, w_gate, w_up, H), s));
+  return gemm(layer, routed_down(layer, T, offsets, H, w_down, y_perm), s);
+}
+
+int moe_shared_ffn(const moe_layer* layer, int64_t T, const void* x, const void* ws_gate,
+                   const void* ws_up, const void* ws_down, void* y_shared, void* ws,
+                   size_t ws_bytes, void* stream) {
+  MOE_TRY(check_layer(layer, T));
+  MOE_TRY(needT(y_shared, T));
+  MOE_TRY(need(ws));
+  if (layer->n_shared > 0) {
+    MOE_TRY(needT(x, T));
+    MOE_TRY(need(ws_gate));
+    MOE_TRY(need(ws_up));
+    MOE_TRY(need(ws_down));
+  }
+  const Layout lo = layout_of(layer, T);
+  if (ws_bytes < lo.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (layer->n_shared == 0) {
+    MOE_HIP(moe::launch_zero(y_shared, static_cast<size_t>(T) * layer->d_model * elt_bytes(layer), s));
+    return MOE_OK;
+  }
+  return run_shared(layer, T, x, ws_gate, ws_up, ws_down, y_shared, at(ws, lo.h_shared), s);
+}
+
+int moe_combine(const moe_layer* layer, int64_t T, const void* y_perm, const int32_t* slot_row,
+                const float* topk_w, const void* y_shared, const void* residual, void* y,
+                void* stream) {
+  MOE_TRY(check_layer(layer, T));
+  MOE_TRY(needT(y_perm, T));
+  MOE_TRY(needT(slot_row, T));
+  MOE_TRY(needT(topk_w, T));
+  MOE_TRY(opt(y_shared));
+  MOE_TRY(opt(residual));
+  MOE_TRY(needT(y, T));
+  if (T == 0) return MOE_OK;
+  moe::CombineArgs a{};
+  a.y_perm = y_perm;
+  a.slot_row = slot_row;
+  a.topk_w = topk_w;
+  a.y_shared = y_shared;
+  a.residual = residual;
+  a.y = y;
+  a.T = static_cast<int>(T);
+  a.d = layer->d_model;
+  a.top_k = layer->top_k;
+  a.bf16 = layer->dtype == MOE_BF16;
+  MOE_HIP(moe::launch_combine(a, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+int moe_forward(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
+                const float* logit_bias, const void* w_gate, const void* w_up,
+                const void* w_down, const void* ws_gate, const void* ws_up,
+                const void* ws_down, const void* residual, void* y, int32_t* topk_idx,
+                float* topk_w, int32_t* counts, int32_t* offsets, void* ws, size_t ws_bytes,
+                void* stream) {
+  MOE_TRY(check_layer(layer, T));
+  MOE_TRY(needT(x, T));
+  MOE_TRY(need(w_router));
+  MOE_TRY(opt(logit_bias));
+  MOE_TRY(need(w_gate));
+  MOE_TRY(need(w_up));
+  MOE_TRY(need(w_down));
+  if (layer->n_shared > 0) {
+    MOE_TRY(need(ws_gate));
+    MOE_TRY(need(ws_up));
+    MOE_TRY(need(ws_down));
+  }
+  MOE_TRY(opt(residual));
+  MOE_TRY(needT(y, T));
+  MOE_TRY(opt(topk_idx));
+  MOE_TRY(opt(topk_w));
+  MOE_TRY(opt(counts));
+  MOE_TRY(opt(offsets));
+  MOE_TRY(need(ws));
+  const Layout lo = layout_of(layer, T);
+  if (ws_bytes < lo.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (topk_idx == nullptr) topk_idx = reinterpret_cast<int32_t*>(at(ws, lo.topk_idx));
+  if (topk_w == nullptr) topk_w = reinterpret_cast<float*>(at(ws, lo.topk_w));
+  if (counts == nullptr) counts = reinterpret_cast<int32_t*>(at(ws, lo.counts));
+  if (offsets == nullptr) offsets = reinterpret_cast<int32_t*>(at(ws, lo.offsets));
+  if (T == 0) {
+    MOE_TRY(permute_impl(layer, T, nullptr, nullptr, counts, offsets, nullptr, nullptr, nullptr,
+                         ws, lo, s));
+    return MOE_OK;
+  }
+  int32_t* row_token = reinterpret_cast<int32_t*>(at(ws, lo.row_token));
+  int32_t* slot_row = reinterpret_cast<int32_t*>(at(ws, lo.slot_row));
+  void* H = at(ws, lo.h);
+  void* y_perm = at(ws, lo.y_perm);
+  void* y_shared = layer->n_shared > 0 ? at(ws, lo.y_shared) : nullptr;
+
+  MOE_TRY(moe_route(layer, T, x, w_router, logit_bias, topk_idx, topk_w, stream));
+  MOE_TRY(permute_impl(layer, T, topk_idx, nullptr, counts, offsets, row_token, slot_row,
+                       nullptr, ws, lo, s));
+  // Routed experts; the gather x[row_token[r]] happens inside the A-tile load.
+  MOE_TRY(gemm(layer, routed_gate_up(layer, T, offsets, x, row_token, w_gate, w_up, H), s));
+  MOE_TRY(gemm(layer, routed_down(layer, T, offsets, H, w_down, y_perm), s));
+  if (layer->n_shared > 0)
+    MOE_TRY(run_shared(layer, T, x, ws_gate, ws_up, ws_down, y_shared, at(ws, lo.h_shared), s));
+  return moe_combine(layer, T, y_perm, slot_row, topk_w, y_shared, residual, y, stream);
+}
+
+}  // extern "C"

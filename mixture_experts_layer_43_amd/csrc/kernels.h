@@ -1,0 +1,80 @@
+// Internal launch interface between the C-ABI layer (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- router (router.hip) ----
+struct RouteArgs {
+  const void* x;           // [T, d] f32 or bf16
+  const float* w_router;   // [N_r, d]
+  const float* bias;       // [N_r] or null
+  int T, d, n_routed, top_k, gate;
+  bool x_bf16;
+  int32_t* topk_idx;       // [T, K']
+  float* topk_w;           // [T, K']
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+
+// ---- dispatch (dispatch.hip) ----
+constexpr int kCountBlock = 256;  // tokens per counting block
+struct PermuteArgs {
+  const int32_t* topk_idx;  // [T, K']
+  const void* x;            // [T, d] (only when x_perm != null)
+  int T, d, n_routed, top_k, elt_bytes;
+  int32_t* counts;          // [N_r]
+  int32_t* offsets;         // [N_r + 1]
+  int32_t* row_token;       // [P]
+  int32_t* slot_row;        // [P]
+  void* x_perm;             // [P, d] or null
+  int32_t* block_counts;    // ws: [NB, N_r]
+  int32_t* block_base;      // ws: [NB, N_r]
+  int32_t* local_rank;      // ws: [P]
+};
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+
+// ---- grouped GEMMs (gemm_bf16.hip, gemm_f32.hip) ----
+enum GemmMode { kGateUp = 0, kDown = 1 };
+
+// Rows of group g are [offsets[g], offsets[g+1]) of a row-concatenated
+// matrix (offsets null: one group of M rows).  A row r lives at
+// A + (gather ? gather[r] : r) * lda.  B element (n, k) of group g is
+// B + g*b_group_stride + (k / k_sub)*b_sub_stride + n*ldb + (k % k_sub).
+// kGateUp: C[r, n] = silu(A_r . B0_n) * (A_r . B1_n), n < N.
+// kDown:   C[r, n] = A_r . B0_n.
+struct GemmArgs {
+  const int32_t* offsets;
+  int n_groups;
+  int64_t rows_total;      // sum of group rows (host known: P or T)
+  const void* A;
+  int64_t lda;
+  const int32_t* gather;
+  const void* B0;
+  const void* B1;
+  int64_t ldb, b_group_stride, b_sub_stride;
+  int k_sub;
+  int N, K;
+  void* C;
+  int64_t ldc;
+  int mode;
+};
+hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
+
+// ---- combine (combine.hip) ----
+struct CombineArgs {
+  const void* y_perm;       // [P, d]
+  const int32_t* slot_row;  // [P]
+  const float* topk_w;      // [T, K']
+  const void* y_shared;     // [T, d] or null
+  const void* residual;     // [T, d] or null
+  void* y;                  // [T, d]
+  int T, d, top_k;
+  bool bf16;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+
+}  // namespace moe
