@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""DeepSeekMoE layer forward on one MI355X: tokens/s and expert-GEMM TFLOP/s.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload 16b]
+
+A step is one moe_forward (router, dispatch, routed gate/up and down grouped
+GEMMs, shared experts, combine) over one batch of seeded synthetic inputs
+that are resident in HBM before timing starts.  The timed steps run through
+moe_forward_timed, which records a HIP event pair around every stage on the
+launch stream, so per-stage GPU times come from the timed region itself.
+
+Prints one JSON line.  `roofline` is for the dominant kernel, the routed
+gate/up grouped GEMM: algorithmic FLOPs 4*P*d*I per launch (P = T*K'
+assignments) over its event-timed duration, against the bf16 dense MFMA
+peak.  `cpu_baseline` times the fp64 oracle on the first --cpu-tokens tokens
+of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+# rocprofv3 FETCH_SIZE / WRITE_SIZE of the routed gate/up kernel on this workload,
+# already divided by the copy-kernel calibration factor; None until measured
+# for the current kernel.
+TRAFFIC_BYTES = None
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="16b", help="layer shape from synth.configs")
+    ap.add_argument("--cpu-tokens", type=int, default=8192,
+                    help="tokens of the workload the oracle is timed on (0: skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for counter scaling)")
+    return ap.parse_args()
+
+
+def hip_runtime():
+    h = ctypes.CDLL("libamdhip64.so")
+    h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return h
+
+
+def upload(a, device):
+    import numpy as np
+    import torch
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(a).to(device)
+
+
+def cpu_baseline(cfg, inputs, n_tokens):
+    """The fp64 oracle, as it stands, on the first n_tokens tokens of the workload."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    n = min(n_tokens, cfg.tokens)
+    sub = dict(inputs)
+    sub["x"] = inputs["x"][:n]
+    c = cfg.with_(tokens=n)
+    t0 = time.perf_counter()
+    oracle.forward(c, sub)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {cfg.tokens} tokens of the same layer, fp64 numpy "
+                      f"(routing + dispatch + all chosen experts + shared + combine), "
+                      f"{dt:.2f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer is run and timed on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from mixture_experts_layer_43_amd import _lib, ops
+    from synth import get_config, make_inputs
+
+    cfg = get_config(args.workload)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    t_gen = time.perf_counter()
+    inputs = make_inputs(cfg)
+    d = {k: upload(v, dev) for k, v in inputs.items()}
+    torch.cuda.synchronize()
+    print(f"[bench] inputs for {cfg.name} ready in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
+
+    lay = ops.Layer.of(cfg)
+    fwd = ops.Forward(lay, cfg.tokens, dev)
+    fwd.check(d["x"], d["w_router"], d["bias"], d["w_gate"], d["w_up"], d["w_down"],
+              d["ws_gate"], d["ws_up"], d["ws_down"], None)
+    call_args = [d["x"], d["w_router"], d["bias"], d["w_gate"], d["w_up"], d["w_down"],
+                 d["ws_gate"], d["ws_up"], d["ws_down"]]
+
+    for _ in range(args.warmup):
+        fwd(*call_args, checked=True)
+    torch.cuda.synchronize()
+
+    hip = hip_runtime()
+    nev = 2 * _lib.MOE_NUM_STAGES
+    events = []
+    for _ in range(args.steps):
+        arr = (ctypes.c_void_p * nev)()
+        for i in range(nev):
+            ev = ctypes.c_void_p()
+            assert hip.hipEventCreate(ctypes.byref(ev)) == 0
+            arr[i] = ev.value
+        events.append(arr)
+
+    p = ops._p
+    lib = _lib.lib()
+    c_layer = lay.c()
+    stream = ops._stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for k in range(args.steps):
+        _lib.check("moe_forward_timed", lib.moe_forward_timed(
+            ctypes.byref(c_layer), cfg.tokens, p(d["x"]), p(d["w_router"]), p(d["bias"]),
+            p(d["w_gate"]), p(d["w_up"]), p(d["w_down"]), p(d["ws_gate"]), p(d["ws_up"]),
+            p(d["ws_down"]), None, p(fwd.y), p(fwd.topk_idx), p(fwd.topk_w), p(fwd.counts),
+            p(fwd.offsets), p(fwd.ws), fwd.ws.numel(), stream, events[k]))
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms = total_ms / args.steps
+
+    stage_ms = np.zeros((args.steps, _lib.MOE_NUM_STAGES))
+    f = ctypes.c_float()
+    for k, arr in enumerate(events):
+        for s in range(_lib.MOE_NUM_STAGES):
+            assert hip.hipEventElapsedTime(ctypes.byref(f), arr[2 * s], arr[2 * s + 1]) == 0
+            stage_ms[k, s] = f.value
+        for i in range(nev):
+            hip.hipEventDestroy(arr[i])
+    st = dict(zip(_lib.STAGES, stage_ms.mean(0).round(5).tolist()))
+
+    T, dm, I, K = cfg.tokens, cfg.d_model, cfg.d_ff, cfg.top_k
+    P = T * K
+    gu_flop = 4.0 * P * dm * I
+    dn_flop = 2.0 * P * dm * I
+    sh_flop = 6.0 * T * dm * cfg.n_shared * cfg.d_ff_shared
+    router_flop = 2.0 * T * dm * cfg.n_routed
+    gu_ms = st["routed_gate_up"]
+    expert_ms = st["routed_gate_up"] + st["routed_down"]
+    gu_tflops = gu_flop / (gu_ms * 1e-3) / 1e12
+    expert_tflops = (gu_flop + dn_flop) / (expert_ms * 1e-3) / 1e12
+    layer_tflops = (gu_flop + dn_flop + sh_flop + router_flop) / (ms * 1e-3) / 1e12
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    out = {
+        "metric": "MoE-layer fwd tokens/sec + expert GEMM TFLOP/s (% MFMA peak), 16B-shape layer",
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"DeepSeekMoE {cfg.name} layer forward: T={T}, d={dm}, "
+                        f"{cfg.n_routed} routed (top-{K}) + {cfg.n_shared} shared experts, "
+                        f"SiLU FFN width {I}, {cfg.gate}",
+            "tokens": T, "d_model": dm, "n_routed": cfg.n_routed, "n_shared": cfg.n_shared,
+            "top_k": K, "d_ff": I, "gate": cfg.gate, "parallelism": "single GPU",
+        },
+        "expert_gemm_tflops": expert_tflops,
+        "expert_gemm_frac_mfma": expert_tflops / PEAK_BF16_TFLOPS,
+        "layer_tflops": layer_tflops,
+        "stage_ms": st,
+        "roofline": {
+            "kernel": "routed gate/up grouped GEMM (grouped_gemm_bf16 gate/up, grouped)",
+            "bound": "mfma",
+            "achieved": gu_tflops,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": gu_tflops / PEAK_BF16_TFLOPS,
+            "traffic": TRAFFIC_BYTES,
+            "algorithmic_flop_per_launch": gu_flop,
+            "avg_launch_ms": gu_ms,
+        },
+    }
+    if args.cpu_tokens > 0:
+        print("[bench] timing the fp64 oracle on the host", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cfg, inputs, args.cpu_tokens)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

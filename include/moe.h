@@ -148,6 +148,31 @@ int moe_forward(const moe_layer* layer, int64_t T, const void* x, const float* w
                 float* topk_w, int32_t* counts, int32_t* offsets, void* ws, size_t ws_bytes,
                 void* stream);
 
+/* Stages of moe_forward, in launch order. */
+#define MOE_NUM_STAGES 7
+enum {
+  MOE_STAGE_ROUTE = 0,          /* router logits, softmax, top-K'             */
+  MOE_STAGE_DISPATCH = 1,       /* histogram, scan, scatter of row indices    */
+  MOE_STAGE_ROUTED_GATE_UP = 2, /* grouped GEMM x W1/W3 + silu(gate) * up     */
+  MOE_STAGE_ROUTED_DOWN = 3,    /* grouped GEMM H W2                          */
+  MOE_STAGE_SHARED_GATE_UP = 4, /* shared experts, width K_s*I_s (empty if 0) */
+  MOE_STAGE_SHARED_DOWN = 5,
+  MOE_STAGE_COMBINE = 6
+};
+
+/* moe_forward with per-stage timing markers, for measurement.  `events`
+ * holds 2*MOE_NUM_STAGES hipEvent_t handles (as void*) created by the caller;
+ * events[2s] and events[2s+1] are recorded on `stream` right before and
+ * right after stage s, so hipEventElapsedTime(events[2s], events[2s+1]) is
+ * that stage's GPU time.  A NULL array or handle is MOE_ERR_INVALID_ARG.
+ * Everything else is exactly moe_forward. */
+int moe_forward_timed(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
+                      const float* logit_bias, const void* w_gate, const void* w_up,
+                      const void* w_down, const void* ws_gate, const void* ws_up,
+                      const void* ws_down, const void* residual, void* y, int32_t* topk_idx,
+                      float* topk_w, int32_t* counts, int32_t* offsets, void* ws,
+                      size_t ws_bytes, void* stream, void* const* events);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,8 +14,11 @@ MOE_GATE_SOFTMAX_TOPK, MOE_GATE_TOPK_SOFTMAX = 0, 1
 EXPORTS = (
     "moe_abi_version", "moe_status_str", "moe_last_hip_error", "moe_workspace_size",
     "moe_route", "moe_permute", "moe_expert_ffn", "moe_shared_ffn", "moe_combine",
-    "moe_forward",
+    "moe_forward", "moe_forward_timed",
 )
+MOE_NUM_STAGES = 7
+STAGES = ("route", "dispatch", "routed_gate_up", "routed_down", "shared_gate_up", "shared_down",
+          "combine")
 
 
 class MoeLayer(ctypes.Structure):
@@ -49,6 +52,8 @@ _SIGS = {
     "moe_shared_ffn": ([LP, I64, P, P, P, P, P, P, SZ, P], ctypes.c_int),
     "moe_combine": ([LP, I64, P, P, P, P, P, P, P], ctypes.c_int),
     "moe_forward": ([LP, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
+    "moe_forward_timed": ([LP, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P,
+                           ctypes.POINTER(ctypes.c_void_p)], ctypes.c_int),
 }
 
 

@@ -55,6 +55,11 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    # A kernel whose host stub was not emitted links fine but fails at load.
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in nm.stdout.splitlines() if "device_stub" in l]
+    if missing:
+        raise RuntimeError("kernel host stubs missing from libmoe.so:\n" + "\n".join(missing))
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB} from {len(srcs)} sources", file=sys.stderr)

@@ -147,9 +147,9 @@ int gemm(const moe_layer* L, const moe::GemmArgs& g, hipStream_t s) {
   return MOE_OK;
 }
 
-int run_shared(const moe_layer* L, int64_t T, const void* x, const void* ws_gate,
-               const void* ws_up, const void* ws_down, void* y_shared, void* h_shared,
-               hipStream_t s) {
+// Shared experts as one FFN of width K_s*I_s: [K_s, I_s, d] is [K_s*I_s, d].
+moe::GemmArgs shared_gate_up(const moe_layer* L, int64_t T, const void* x, const void* ws_gate,
+                             const void* ws_up, void* h_shared) {
   const int wsh = L->n_shared * L->d_ff_shared;
   moe::GemmArgs g{};
   g.offsets = nullptr;
@@ -157,7 +157,7 @@ int run_shared(const moe_layer* L, int64_t T, const void* x, const void* ws_gate
   g.rows_total = T;
   g.A = x;
   g.lda = L->d_model;
-  g.B0 = ws_gate;  // [K_s, I_s, d] is [K_s*I_s, d]: one FFN of width K_s*I_s
+  g.B0 = ws_gate;
   g.B1 = ws_up;
   g.ldb = L->d_model;
   g.k_sub = L->d_model;
@@ -166,14 +166,20 @@ int run_shared(const moe_layer* L, int64_t T, const void* x, const void* ws_gate
   g.C = h_shared;
   g.ldc = wsh;
   g.mode = moe::kGateUp;
-  MOE_TRY(gemm(L, g, s));
+  return g;
+}
+
+// The down projection's K runs over the K_s matrices [d, I_s] in turn.
+moe::GemmArgs shared_down(const moe_layer* L, int64_t T, const void* h_shared,
+                          const void* ws_down, void* y_shared) {
+  const int wsh = L->n_shared * L->d_ff_shared;
   moe::GemmArgs h{};
   h.offsets = nullptr;
   h.n_groups = 1;
   h.rows_total = T;
   h.A = h_shared;
   h.lda = wsh;
-  h.B0 = ws_down;  // K runs over the K_s matrices [d, I_s] in turn
+  h.B0 = ws_down;
   h.ldb = L->d_ff_shared;
   h.k_sub = L->d_ff_shared;
   h.b_sub_stride = static_cast<int64_t>(L->d_model) * L->d_ff_shared;
@@ -182,8 +188,18 @@ int run_shared(const moe_layer* L, int64_t T, const void* x, const void* ws_gate
   h.C = y_shared;
   h.ldc = L->d_model;
   h.mode = moe::kDown;
-  return gemm(L, h, s);
+  return h;
 }
+
+// Optional stage markers for moe_forward_timed.
+struct Marks {
+  hipEvent_t const* ev;
+  hipStream_t s;
+  int mark(int i) const {
+    if (ev != nullptr) MOE_HIP(hipEventRecord(ev[i], s));
+    return MOE_OK;
+  }
+};
 
 }  // namespace
 
@@ -318,7 +334,9 @@ int moe_shared_ffn(const moe_layer* layer, int64_t T, const void* x, const void*
     MOE_HIP(moe::launch_zero(y_shared, static_cast<size_t>(T) * layer->d_model * elt_bytes(layer), s));
     return MOE_OK;
   }
-  return run_shared(layer, T, x, ws_gate, ws_up, ws_down, y_shared, at(ws, lo.h_shared), s);
+  void* hs = at(ws, lo.h_shared);
+  MOE_TRY(gemm(layer, shared_gate_up(layer, T, x, ws_gate, ws_up, hs), s));
+  return gemm(layer, shared_down(layer, T, hs, ws_down, y_shared), s);
 }
 
 int moe_combine(const moe_layer* layer, int64_t T, const void* y_perm, const int32_t* slot_row,
@@ -347,12 +365,12 @@ int moe_combine(const moe_layer* layer, int64_t T, const void* y_perm, const int
   return MOE_OK;
 }
 
-int moe_forward(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
-                const float* logit_bias, const void* w_gate, const void* w_up,
-                const void* w_down, const void* ws_gate, const void* ws_up,
-                const void* ws_down, const void* residual, void* y, int32_t* topk_idx,
-                float* topk_w, int32_t* counts, int32_t* offsets, void* ws, size_t ws_bytes,
-                void* stream) {
+static int forward_impl(const moe_layer* layer, int64_t T, const void* x,
+                        const float* w_router, const float* logit_bias, const void* w_gate,
+                        const void* w_up, const void* w_down, const void* ws_gate,
+                        const void* ws_up, const void* ws_down, const void* residual, void* y,
+                        int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                        void* ws, size_t ws_bytes, void* stream, hipEvent_t const* events) {
   MOE_TRY(check_layer(layer, T));
   MOE_TRY(needT(x, T));
   MOE_TRY(need(w_router));
@@ -375,30 +393,73 @@ int moe_forward(const moe_layer* layer, int64_t T, const void* x, const float* w
   const Layout lo = layout_of(layer, T);
   if (ws_bytes < lo.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const Marks m{events, s};
   if (topk_idx == nullptr) topk_idx = reinterpret_cast<int32_t*>(at(ws, lo.topk_idx));
   if (topk_w == nullptr) topk_w = reinterpret_cast<float*>(at(ws, lo.topk_w));
   if (counts == nullptr) counts = reinterpret_cast<int32_t*>(at(ws, lo.counts));
   if (offsets == nullptr) offsets = reinterpret_cast<int32_t*>(at(ws, lo.offsets));
   if (T == 0) {
-    MOE_TRY(permute_impl(layer, T, nullptr, nullptr, counts, offsets, nullptr, nullptr, nullptr,
-                         ws, lo, s));
-    return MOE_OK;
+    for (int i = 0; i < 2 * MOE_NUM_STAGES; ++i) MOE_TRY(m.mark(i));
+    return permute_impl(layer, T, nullptr, nullptr, counts, offsets, nullptr, nullptr, nullptr,
+                        ws, lo, s);
   }
   int32_t* row_token = reinterpret_cast<int32_t*>(at(ws, lo.row_token));
   int32_t* slot_row = reinterpret_cast<int32_t*>(at(ws, lo.slot_row));
   void* H = at(ws, lo.h);
   void* y_perm = at(ws, lo.y_perm);
+  void* h_shared = at(ws, lo.h_shared);
   void* y_shared = layer->n_shared > 0 ? at(ws, lo.y_shared) : nullptr;
 
+  MOE_TRY(m.mark(0));
   MOE_TRY(moe_route(layer, T, x, w_router, logit_bias, topk_idx, topk_w, stream));
+  MOE_TRY(m.mark(1));
+  MOE_TRY(m.mark(2));
   MOE_TRY(permute_impl(layer, T, topk_idx, nullptr, counts, offsets, row_token, slot_row,
                        nullptr, ws, lo, s));
+  MOE_TRY(m.mark(3));
   // Routed experts; the gather x[row_token[r]] happens inside the A-tile load.
+  MOE_TRY(m.mark(4));
   MOE_TRY(gemm(layer, routed_gate_up(layer, T, offsets, x, row_token, w_gate, w_up, H), s));
+  MOE_TRY(m.mark(5));
+  MOE_TRY(m.mark(6));
   MOE_TRY(gemm(layer, routed_down(layer, T, offsets, H, w_down, y_perm), s));
+  MOE_TRY(m.mark(7));
+  MOE_TRY(m.mark(8));
   if (layer->n_shared > 0)
-    MOE_TRY(run_shared(layer, T, x, ws_gate, ws_up, ws_down, y_shared, at(ws, lo.h_shared), s));
-  return moe_combine(layer, T, y_perm, slot_row, topk_w, y_shared, residual, y, stream);
+    MOE_TRY(gemm(layer, shared_gate_up(layer, T, x, ws_gate, ws_up, h_shared), s));
+  MOE_TRY(m.mark(9));
+  MOE_TRY(m.mark(10));
+  if (layer->n_shared > 0)
+    MOE_TRY(gemm(layer, shared_down(layer, T, h_shared, ws_down, y_shared), s));
+  MOE_TRY(m.mark(11));
+  MOE_TRY(m.mark(12));
+  MOE_TRY(moe_combine(layer, T, y_perm, slot_row, topk_w, y_shared, residual, y, stream));
+  return m.mark(13);
+}
+
+int moe_forward(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
+                const float* logit_bias, const void* w_gate, const void* w_up,
+                const void* w_down, const void* ws_gate, const void* ws_up,
+                const void* ws_down, const void* residual, void* y, int32_t* topk_idx,
+                float* topk_w, int32_t* counts, int32_t* offsets, void* ws, size_t ws_bytes,
+                void* stream) {
+  return forward_impl(layer, T, x, w_router, logit_bias, w_gate, w_up, w_down, ws_gate, ws_up,
+                      ws_down, residual, y, topk_idx, topk_w, counts, offsets, ws, ws_bytes,
+                      stream, nullptr);
+}
+
+int moe_forward_timed(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
+                      const float* logit_bias, const void* w_gate, const void* w_up,
+                      const void* w_down, const void* ws_gate, const void* ws_up,
+                      const void* ws_down, const void* residual, void* y, int32_t* topk_idx,
+                      float* topk_w, int32_t* counts, int32_t* offsets, void* ws,
+                      size_t ws_bytes, void* stream, void* const* events) {
+  if (events == nullptr) return MOE_ERR_INVALID_ARG;
+  for (int i = 0; i < 2 * MOE_NUM_STAGES; ++i)
+    if (events[i] == nullptr) return MOE_ERR_INVALID_ARG;
+  return forward_impl(layer, T, x, w_router, logit_bias, w_gate, w_up, w_down, ws_gate, ws_up,
+                      ws_down, residual, y, topk_idx, topk_w, counts, offsets, ws, ws_bytes,
+                      stream, reinterpret_cast<hipEvent_t const*>(events));
 }
 
 }  // extern "C"

@@ -12,10 +12,10 @@
 // packs BN/2 rows of W1 and the same BN/2 rows of W3 into one B tile, so a
 // wavefront holds matching gate and up accumulators and applies
 // silu(gate) * up in registers before the single bf16 store of H.  Down mode
-// is a plain A . B^T.  Operands go global -> registers -> LDS (two stages,
-// 16-byte chunks, XOR-swizzled rows so the 16-byte fragment reads of a
-// quarter-wave hit distinct banks) -> v_mfma_f32_32x32x16_bf16, fp32
-// accumulation.  Workgroup ids are remapped so that consecutive tiles run on
+// is a plain A . B^T.  Operands go global -> LDS directly
+// (global_load_lds_dwordx4, no staging registers; two stages; 16-byte chunks
+// in XOR-swizzled rows so the 16-byte fragment reads of a quarter-wave hit
+// distinct banks) -> v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  Workgroup ids are remapped so that consecutive tiles run on
 // the same XCD and share its L2.
 #include "common.h"
 #include "kernels.h"
@@ -29,6 +29,17 @@ constexpr int kChunks = BK / 8; // 16-byte chunks per row
 constexpr int kXcds = 8;
 constexpr int kMaxGroups = 256;
 
+// 16 bytes per lane from global memory straight into LDS (the 64 lanes of the
+// wavefront fill 1 KB starting at the wave-uniform address lds).
+__device__ __forceinline__ void copy_to_lds16(const bf16_t* src, bf16_t* lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
+
+// silu(a) = a * sigmoid(a) with the hardware reciprocal (epilogue only).
+__device__ __forceinline__ float silu_fast(float a) {
+  return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a));
+}
+
 // 16-byte chunk c of tile row r is stored at chunk position c ^ swz(r).
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
@@ -40,7 +51,9 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return xcd * base + min(xcd, rem) + local;
 }
 
-template <int BM, int BN, int WM, int WN, int MODE>
+// GROUPED: rows come in per-expert groups described by offsets (routed
+// experts); otherwise one dense group (shared experts).
+template <int BM, int BN, int WM, int WN, int MODE, bool GROUPED>
 __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p) {
   constexpr int NT = WM * WN * kWave;
   constexpr int TM = BM / WM;               // rows per wavefront
@@ -48,9 +61,10 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
   constexpr int MB = TM / 32;
   constexpr int NB = TN / 32;
   constexpr int OUT_N = (MODE == kGateUp) ? BN / 2 : BN;
-  constexpr int A_LOADS = BM * kChunks / NT;
-  constexpr int B_LOADS = BN * kChunks / NT;
-  static_assert(BM * kChunks % NT == 0 && BN * kChunks % NT == 0, "tile/thread mismatch");
+  constexpr int NW = WM * WN;
+  constexpr int A_LD = BM / 8 / NW;         // 8-row LDS loads per wavefront per K step
+  constexpr int B_LD = BN / 8 / NW;
+  static_assert(A_LD * 8 * NW == BM && B_LD * 8 * NW == BN, "tile/wave mismatch");
   static_assert(MODE == kDown || NB % 2 == 0, "gate/up needs paired blocks");
 
   __shared__ __attribute__((aligned(16))) bf16_t smem[2][(BM + BN) * BK];
@@ -69,7 +83,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
 
   // ---- locate (group, first row, rows) of row tile mt ------------------
   int g, row0, rows;
-  if (p.offsets == nullptr) {
+  if (!GROUPED) {
     g = 0;
     row0 = mt * BM;
     rows = static_cast<int>(min<int64_t>(BM, p.rows_total - row0));
@@ -110,24 +124,28 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
                          ? static_cast<const bf16_t*>(p.B1) + static_cast<int64_t>(g) * p.b_group_stride
                          : nullptr;
 
-  // ---- per-thread global chunk pointers (fixed over K) -------------------
-  const bf16_t* a_src[A_LOADS];
-  int a_lds[A_LOADS];
+  // ---- per-lane source chunks (fixed over K) -----------------------------
+  // One global_load_lds_dwordx4 moves 64 lanes x 16 B into a contiguous 1 KB
+  // of LDS: 8 tile rows of one K step.  Lane L lands on row L/8, chunk
+  // position L%8, so it fetches logical chunk (L%8) ^ swz(row): the load
+  // itself writes the swizzled layout.
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int lr = lane >> 3;
+  const int lp = lane & 7;
+  const bf16_t* a_src[A_LD];
 #pragma unroll
-  for (int i = 0; i < A_LOADS; ++i) {
-    const int ch = tid + i * NT;
-    const int r = ch / kChunks, c = ch % kChunks;
+  for (int i = 0; i < A_LD; ++i) {
+    const int r = (wv * A_LD + i) * 8 + lr;
+    const int c = lp ^ swz(r);
     const int64_t grow = row0 + min(r, rows - 1);
     const int64_t arow = p.gather ? p.gather[grow] : grow;
     a_src[i] = A + arow * p.lda + c * 8;
-    a_lds[i] = r * BK + ((c ^ swz(r)) * 8);
   }
-  const bf16_t* b_src[B_LOADS];
-  int b_lds[B_LOADS];
+  const bf16_t* b_src[B_LD];
 #pragma unroll
-  for (int i = 0; i < B_LOADS; ++i) {
-    const int ch = tid + i * NT;
-    const int r = ch / kChunks, c = ch % kChunks;
+  for (int i = 0; i < B_LD; ++i) {
+    const int r = (wv * B_LD + i) * 8 + lr;
+    const int c = lp ^ swz(r);
     const bf16_t* base;
     int n;
     if (MODE == kGateUp) {
@@ -140,24 +158,18 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
     }
     n = min(n, p.N - 1);
     b_src[i] = base + static_cast<int64_t>(n) * p.ldb + c * 8;
-    b_lds[i] = BM * BK + r * BK + ((c ^ swz(r)) * 8);
   }
 
-  uint4 a_reg[A_LOADS], b_reg[B_LOADS];
-  auto load_tile = [&](int kt) {
+  // Asynchronous global -> LDS copy of K step kt into stage buffer s.
+  auto issue = [&](int kt, bf16_t* s) {
     const int k = kt * BK;
     const int64_t boff = static_cast<int64_t>(k / p.k_sub) * p.b_sub_stride + (k % p.k_sub);
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) a_reg[i] = *reinterpret_cast<const uint4*>(a_src[i] + k);
+    for (int i = 0; i < A_LD; ++i)
+      copy_to_lds16(a_src[i] + k, s + (wv * A_LD + i) * 8 * BK);
 #pragma unroll
-    for (int i = 0; i < B_LOADS; ++i) b_reg[i] = *reinterpret_cast<const uint4*>(b_src[i] + boff);
-  };
-  auto store_tile = [&](int stage) {
-    bf16_t* s = smem[stage];
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) *reinterpret_cast<uint4*>(s + a_lds[i]) = a_reg[i];
-#pragma unroll
-    for (int i = 0; i < B_LOADS; ++i) *reinterpret_cast<uint4*>(s + b_lds[i]) = b_reg[i];
+    for (int i = 0; i < B_LD; ++i)
+      copy_to_lds16(b_src[i] + boff, s + BM * BK + (wv * B_LD + i) * 8 * BK);
   };
 
   f32x16 acc[MB][NB];
@@ -185,33 +197,45 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
     }
   }
 
+  // Per K step: read every fragment of the current stage into registers,
+  // then start the asynchronous copy of the next step into the other stage
+  // (issued after the reads, so no wait on the copy is needed before them),
+  // then run the step's MFMAs while the copy is in flight.
   const int nk = p.K / BK;
-  load_tile(0);
-  store_tile(0);
+  issue(0, smem[0]);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-
   for (int kt = 0; kt < nk; ++kt) {
     const int stage = kt & 1;
-    if (kt + 1 < nk) load_tile(kt + 1);
     const bf16_t* s = smem[stage];
+    bf16x8 af[BK / 16][MB], bfr[BK / 16][NB];
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       const int c = kk * 2 + khalf;
-      bf16x8 af[MB], bfr[NB];
 #pragma unroll
       for (int i = 0; i < MB; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(s + a_row[i] * BK + ((c ^ swz(a_row[i])) * 8));
+        af[kk][i] = *reinterpret_cast<const bf16x8*>(s + a_row[i] * BK + ((c ^ swz(a_row[i])) * 8));
 #pragma unroll
       for (int j = 0; j < NB; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(s + BM * BK + b_row[j] * BK +
-                                                  ((c ^ swz(b_row[j])) * 8));
+        bfr[kk][j] = *reinterpret_cast<const bf16x8*>(s + BM * BK + b_row[j] * BK +
+                                                      ((c ^ swz(b_row[j])) * 8));
+      // keep the reads in K order so each slice's MFMAs wait only for it
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Unconditional (the last step re-copies itself, in bounds) so no branch
+    // sits between the fragment reads and the MFMAs that wait on them.
+    issue(min(kt + 1, nk - 1), smem[stage ^ 1]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk)
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
         for (int j = 0; j < NB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) store_tile(stage ^ 1);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk][i], bfr[kk][j], acc[i][j], 0, 0, 0);
+    // the MFMAs stay ahead of the wait for the copy
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
@@ -233,7 +257,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
           const int r = wm * TM + i * 32 + 8 * (v >> 2) + hrow + (v & 3);
           if (r < rows) {
             const float gv = acc[i][j][v], uv = acc[i][j + half][v];
-            C[(row0 + r) * p.ldc + col] = f32_to_bf16(silu_f32(gv) * uv);
+            C[(row0 + r) * p.ldc + col] = f32_to_bf16(silu_fast(gv) * uv);
           }
         }
       }
@@ -269,12 +293,16 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   }
   const int64_t grid = max_mtiles * n_ntiles;
   if (grid == 0) return hipSuccess;
-  if (a.mode == kGateUp)
-    hipLaunchKernelGGL((grouped_gemm_bf16<BM, BN, WM, WN, kGateUp>), dim3(grid),
-                       dim3(WM * WN * kWave), 0, s, a);
+  const dim3 block(WM * WN * kWave);
+  const bool grouped = a.offsets != nullptr;
+  if (a.mode == kGateUp && grouped)
+    hipLaunchKernelGGL((grouped_gemm_bf16<BM, BN, WM, WN, kGateUp, true>), dim3(grid), block, 0, s, a);
+  else if (a.mode == kGateUp)
+    hipLaunchKernelGGL((grouped_gemm_bf16<BM, BN, WM, WN, kGateUp, false>), dim3(grid), block, 0, s, a);
+  else if (grouped)
+    hipLaunchKernelGGL((grouped_gemm_bf16<BM, BN, WM, WN, kDown, true>), dim3(grid), block, 0, s, a);
   else
-    hipLaunchKernelGGL((grouped_gemm_bf16<BM, BN, WM, WN, kDown>), dim3(grid),
-                       dim3(WM * WN * kWave), 0, s, a);
+    hipLaunchKernelGGL((grouped_gemm_bf16<BM, BN, WM, WN, kDown, false>), dim3(grid), block, 0, s, a);
   return hipGetLastError();
 }
 
