@@ -5,11 +5,18 @@
 // section 2: Softmax(KeepTopK(H, k)) (noise off) for the second gate kind;
 // section 5: router probabilities are computed in float32.
 //
-// Layout: a wavefront is split into groups of NP lanes; each group owns
-// TPL tokens and lane j of a group owns experts j, j+NP, ... (EPL of them),
-// so the softmax and arg-max over experts are cross-lane reductions inside
-// the group (xor shuffles), and the chosen set is ranked with a ballot.
-// Logits accumulate over d in fp32 with one FMA chain per (token, expert).
+// Logits.  bf16 layers (N_r <= 128) compute x W_g^T on the matrix cores:
+// each fp32 router weight w is split in registers into three bf16 parts
+// hi + mid + lo == w exactly (24 mantissa bits = 3 x 8), every bf16 x bf16
+// product is exact in fp32, and v_mfma_f32_32x32x16_bf16 accumulates the
+// three partial products in fp32, so the logits keep fp32 accuracy at a
+// fraction of the VALU cost.  Other layers use one fp32 FMA chain per
+// (token, expert) on the vector ALUs.
+//
+// Selection: a wavefront is split into groups of NP lanes; lane j of a group
+// owns experts j, j+NP, ... (EPL of them), so the softmax and arg-max over
+// experts are cross-lane reductions inside the group (xor shuffles), and the
+// chosen set is ranked with a ballot.
 #include <math.h>
 
 #include "common.h"
@@ -36,6 +43,60 @@ __device__ __forceinline__ void load4<bf16_t>(const bf16_t* p, float (&v)[4]) {
   v[1] = __uint_as_float(q.x & 0xFFFF0000u);
   v[2] = __uint_as_float(q.y << 16);
   v[3] = __uint_as_float(q.y & 0xFFFF0000u);
+}
+
+// Top-K' of one token's logits z (lane-per-expert inside a group of NP
+// lanes, EPL experts per lane: expert e[q] = lane-in-group + NP*q), gate
+// values, and the ascending-id store.  K' rounds of group arg-max, ties to
+// the lower id; softmax over all routed experts (gate 0) or over the chosen
+// ones (gate 1), both relative to the largest logit.
+template <int NP, int EPL>
+__device__ __forceinline__ void select_and_store(const float (&z)[EPL], const int (&e)[EPL],
+                                                 const bool (&ev)[EPL], int64_t t, int K,
+                                                 int gate, int grp, int lane,
+                                                 int32_t* __restrict__ topk_idx,
+                                                 float* __restrict__ topk_w) {
+  bool sel[EPL];
+#pragma unroll
+  for (int q = 0; q < EPL; ++q) sel[q] = false;
+  float zmax = -INFINITY;
+  for (int r = 0; r < K; ++r) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < EPL; ++q)
+      if (!sel[q]) m = fmaxf(m, z[q]);
+    m = group_max<NP>(m);
+    if (r == 0) zmax = m;
+    int cand = 0x7FFFFFFF;
+#pragma unroll
+    for (int q = 0; q < EPL; ++q)
+      if (!sel[q] && ev[q] && z[q] == m) cand = min(cand, e[q]);
+    cand = group_min_int<NP>(cand);
+#pragma unroll
+    for (int q = 0; q < EPL; ++q)
+      if (e[q] == cand) sel[q] = true;
+  }
+  float ex[EPL];
+  float part = 0.0f;
+#pragma unroll
+  for (int q = 0; q < EPL; ++q) {
+    ex[q] = ev[q] ? expf(z[q] - zmax) : 0.0f;
+    if (gate == 0 || sel[q]) part += ex[q];
+  }
+  const float denom = group_sum<NP>(part);
+  const uint64_t gmask = (NP == 64) ? ~0ull : (((1ull << NP) - 1ull) << (grp * NP));
+  const uint64_t below = (1ull << lane) - 1ull;
+  int prior = 0;
+#pragma unroll
+  for (int q = 0; q < EPL; ++q) {
+    const uint64_t m = __ballot(sel[q]) & gmask;
+    if (sel[q]) {
+      const int slot = prior + __popcll(m & below);
+      topk_idx[t * K + slot] = e[q];
+      topk_w[t * K + slot] = ex[q] / denom;
+    }
+    prior += __popcll(m);
+  }
 }
 
 template <typename XT, int NP, int EPL>
@@ -99,57 +160,13 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(
 #pragma unroll
   for (int q = 0; q < EPL; ++q) bq[q] = (bias != nullptr && ev[q]) ? bias[e[q]] : 0.0f;
 
-  const uint64_t gmask = (NP == 64) ? ~0ull : (((1ull << NP) - 1ull) << (grp * NP));
-  const uint64_t below = (1ull << lane) - 1ull;
-
-#pragma unroll
   for (int i = 0; i < kTPL; ++i) {
     const int64_t t = tok0 + i;
     if (t >= T) break;  // uniform within the group
     float z[EPL];
-    bool sel[EPL];
 #pragma unroll
-    for (int q = 0; q < EPL; ++q) {
-      z[q] = ev[q] ? acc[i][q] + bq[q] : -INFINITY;
-      sel[q] = false;
-    }
-    // K' rounds of arg-max over the not-yet-chosen experts; ties -> lower id.
-    float zmax = -INFINITY;
-    for (int r = 0; r < K; ++r) {
-      float m = -INFINITY;
-#pragma unroll
-      for (int q = 0; q < EPL; ++q)
-        if (!sel[q]) m = fmaxf(m, z[q]);
-      m = group_max<NP>(m);
-      if (r == 0) zmax = m;
-      int cand = 0x7FFFFFFF;
-#pragma unroll
-      for (int q = 0; q < EPL; ++q)
-        if (!sel[q] && ev[q] && z[q] == m) cand = min(cand, e[q]);
-      cand = group_min_int<NP>(cand);
-#pragma unroll
-      for (int q = 0; q < EPL; ++q)
-        if (e[q] == cand) sel[q] = true;
-    }
-    float ex[EPL];
-    float part = 0.0f;
-#pragma unroll
-    for (int q = 0; q < EPL; ++q) {
-      ex[q] = ev[q] ? expf(z[q] - zmax) : 0.0f;
-      if (gate == 0 || sel[q]) part += ex[q];
-    }
-    const float denom = group_sum<NP>(part);
-    int prior = 0;
-#pragma unroll
-    for (int q = 0; q < EPL; ++q) {
-      const uint64_t m = __ballot(sel[q]) & gmask;
-      if (sel[q]) {
-        const int slot = prior + __popcll(m & below);
-        topk_idx[t * K + slot] = e[q];
-        topk_w[t * K + slot] = ex[q] / denom;
-      }
-      prior += __popcll(m);
-    }
+    for (int q = 0; q < EPL; ++q) z[q] = ev[q] ? acc[i][q] + bq[q] : -INFINITY;
+    select_and_store<NP, EPL>(z, e, ev, t, K, gate, grp, lane, topk_idx, topk_w);
   }
 }
 
@@ -160,6 +177,180 @@ hipError_t launch_t(const RouteArgs& a, hipStream_t s) {
   const int grid = (a.T + tok_per_block - 1) / tok_per_block;
   hipLaunchKernelGGL((router_kernel<XT, NP, EPL>), dim3(grid), dim3(kRouterThreads), 0, s,
                      static_cast<const XT*>(a.x), a.w_router, a.bias, a.T, a.d, a.n_routed,
+                     a.top_k, a.gate, a.topk_idx, a.topk_w);
+  return hipGetLastError();
+}
+
+
+// ---- matrix-core logits (bf16 x) --------------------------------------------
+
+// v == hi + mid + lo exactly, each part a bf16 value held as an fp32 pattern
+// with a zero low half: truncation keeps the top 8 significant bits and the
+// remainders are exact fp32 differences (same sign and binade).
+__device__ __forceinline__ void split3(float v, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  hi = __float_as_uint(v) & 0xFFFF0000u;
+  const float r1 = v - __uint_as_float(hi);
+  mid = __float_as_uint(r1) & 0xFFFF0000u;
+  const float r2 = r1 - __uint_as_float(mid);
+  lo = __float_as_uint(r2) & 0xFFFF0000u;
+}
+
+// High halves of two fp32 patterns -> one packed bf16 pair (lo element first).
+__device__ __forceinline__ uint32_t pack_hi(uint32_t first, uint32_t second) {
+  return __builtin_amdgcn_perm(second, first, 0x07060302u);
+}
+
+template <int MBLK, int NBLK>
+struct RouterFrag {
+  bf16x8 a[MBLK];        // x: 8 consecutive k of one token row
+  float4 w[NBLK][2];     // W_g: 8 consecutive k of one expert row
+};
+
+template <int MBLK, int NBLK>
+__device__ __forceinline__ void router_load(RouterFrag<MBLK, NBLK>& f, const bf16_t* const (&ap)[MBLK],
+                                            const float* const (&bp)[NBLK], int off) {
+#pragma unroll
+  for (int mb = 0; mb < MBLK; ++mb) f.a[mb] = *reinterpret_cast<const bf16x8*>(ap[mb] + off);
+#pragma unroll
+  for (int nb = 0; nb < NBLK; ++nb) {
+    f.w[nb][0] = *reinterpret_cast<const float4*>(bp[nb] + off);
+    f.w[nb][1] = *reinterpret_cast<const float4*>(bp[nb] + off + 4);
+  }
+}
+
+template <int MBLK, int NBLK>
+__device__ __forceinline__ void router_mma(f32x16 (&acc)[MBLK][NBLK], const RouterFrag<MBLK, NBLK>& f,
+                                           const bool (&ev)[NBLK]) {
+#pragma unroll
+  for (int nb = 0; nb < NBLK; ++nb) {
+    const float v[8] = {f.w[nb][0].x, f.w[nb][0].y, f.w[nb][0].z, f.w[nb][0].w,
+                        f.w[nb][1].x, f.w[nb][1].y, f.w[nb][1].z, f.w[nb][1].w};
+    uint32_t h[8], m[8], l[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) split3(ev[nb] ? v[i] : 0.0f, h[i], m[i], l[i]);
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 ph, pm, pl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ph[i] = pack_hi(h[2 * i], h[2 * i + 1]);
+      pm[i] = pack_hi(m[2 * i], m[2 * i + 1]);
+      pl[i] = pack_hi(l[2 * i], l[2 * i + 1]);
+    }
+    const bf16x8 bh = __builtin_bit_cast(bf16x8, ph);
+    const bf16x8 bm = __builtin_bit_cast(bf16x8, pm);
+    const bf16x8 bl = __builtin_bit_cast(bf16x8, pl);
+#pragma unroll
+    for (int mb = 0; mb < MBLK; ++mb) {
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mb], bl, acc[mb][nb], 0, 0, 0);
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mb], bm, acc[mb][nb], 0, 0, 0);
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mb], bh, acc[mb][nb], 0, 0, 0);
+    }
+  }
+}
+
+// One workgroup: 32*MBLK tokens x 32*NBLK experts.  Wavefront w takes the
+// 16-wide K slice w of every 64-wide chunk of d (so each x and W_g element is
+// read once per workgroup), register double-buffered; the four partial
+// logit tiles are summed in LDS in wavefront order (deterministic), then
+// every wavefront selects for its share of the tokens.
+template <int MBLK, int NBLK>
+__global__ __launch_bounds__(kRouterThreads) void router_mfma_kernel(
+    const bf16_t* __restrict__ x, const float* __restrict__ wg, const float* __restrict__ bias,
+    int T, int d, int Nr, int K, int gate, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w) {
+  constexpr int TB = 32 * MBLK;
+  constexpr int NPAD = 32 * NBLK;
+  constexpr int NP = NPAD < kWave ? NPAD : kWave;
+  constexpr int EPL = NPAD / NP;
+  constexpr int G = kWave / NP;
+  constexpr int NW = kRouterThreads / kWave;
+  static_assert((TB / NW) % G == 0, "token split");
+  __shared__ float lg[TB][NPAD + 1];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * TB;
+  const int lr = lane & 31;
+  const int kw = wave * 16 + (lane >> 5) * 8;
+
+  const bf16_t* ap[MBLK];
+#pragma unroll
+  for (int mb = 0; mb < MBLK; ++mb) {
+    const int64_t t = min<int64_t>(tok0 + mb * 32 + lr, T - 1);
+    ap[mb] = x + t * d + kw;
+  }
+  const float* bp[NBLK];
+  bool ev[NBLK];
+#pragma unroll
+  for (int nb = 0; nb < NBLK; ++nb) {
+    const int e = nb * 32 + lr;
+    ev[nb] = e < Nr;
+    bp[nb] = wg + static_cast<int64_t>(min(e, Nr - 1)) * d + kw;
+  }
+
+  f32x16 acc[MBLK][NBLK];
+#pragma unroll
+  for (int mb = 0; mb < MBLK; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NBLK; ++nb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.0f;
+
+  const int nch = d / 64;
+  RouterFrag<MBLK, NBLK> f0, f1;
+  router_load(f0, ap, bp, 0);
+  for (int c = 0; c < nch; c += 2) {
+    if (c + 1 < nch) router_load(f1, ap, bp, (c + 1) * 64);
+    router_mma(acc, f0, ev);
+    if (c + 1 >= nch) break;
+    if (c + 2 < nch) router_load(f0, ap, bp, (c + 2) * 64);
+    router_mma(acc, f1, ev);
+  }
+
+  // D[row][col] of a 32x32 block: lane (col + 32*h), register v, row 8*(v/4) + 4*h + v%4.
+  for (int w = 0; w < NW; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int mb = 0; mb < MBLK; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NBLK; ++nb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int r = mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            const int c = nb * 32 + lr;
+            lg[r][c] = (w == 0) ? acc[mb][nb][v] : lg[r][c] + acc[mb][nb][v];
+          }
+    }
+    __syncthreads();
+  }
+
+  const int grp = lane / NP;
+  const int gl = lane % NP;
+  int e[EPL];
+  bool evq[EPL];
+  float bq[EPL];
+#pragma unroll
+  for (int q = 0; q < EPL; ++q) {
+    e[q] = gl + NP * q;
+    evq[q] = e[q] < Nr;
+    bq[q] = (bias != nullptr && evq[q]) ? bias[e[q]] : 0.0f;
+  }
+  for (int tl = wave * (TB / NW) + grp; tl < (wave + 1) * (TB / NW); tl += G) {
+    const int64_t t = tok0 + tl;
+    if (t >= T) break;  // uniform within the group
+    float z[EPL];
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) z[q] = evq[q] ? lg[tl][e[q]] + bq[q] : -INFINITY;
+    select_and_store<NP, EPL>(z, e, evq, t, K, gate, grp, lane, topk_idx, topk_w);
+  }
+}
+
+template <int MBLK, int NBLK>
+hipError_t launch_mfma(const RouteArgs& a, hipStream_t s) {
+  constexpr int TB = 32 * MBLK;
+  const int grid = (a.T + TB - 1) / TB;
+  hipLaunchKernelGGL((router_mfma_kernel<MBLK, NBLK>), dim3(grid), dim3(kRouterThreads), 0, s,
+                     static_cast<const bf16_t*>(a.x), a.w_router, a.bias, a.T, a.d, a.n_routed,
                      a.top_k, a.gate, a.topk_idx, a.topk_w);
   return hipGetLastError();
 }
@@ -179,6 +370,11 @@ hipError_t launch_x(const RouteArgs& a, hipStream_t s) {
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
+  if (a.x_bf16 && a.d % 64 == 0) {
+    if (a.n_routed <= 32) return launch_mfma<2, 1>(a, s);
+    if (a.n_routed <= 64) return launch_mfma<2, 2>(a, s);
+    if (a.n_routed <= 128) return launch_mfma<1, 4>(a, s);
+  }
   return a.x_bf16 ? launch_x<bf16_t>(a, s) : launch_x<float>(a, s);
 }
 

@@ -33,6 +33,8 @@ MID = {
                            d_ff=40, d_ff_shared=24, dtype="f32", seed=105),
     "mid-wide-k": LayerConfig(name="mid-wide-k", tokens=200, d_model=128, n_routed=100, n_shared=1,
                               top_k=16, d_ff=64, d_ff_shared=64, seed=106),
+    "mid-many-experts": LayerConfig(name="mid-many-experts", tokens=300, d_model=128, n_routed=200,
+                                    n_shared=0, top_k=8, d_ff=64, d_ff_shared=64, seed=107),
 }
 FULL_ORACLE = ["tiny-f32", "16b-decode", *MID]
 SAMPLED = ["2b", "16b", "gshard-zipf"]
@@ -76,7 +78,8 @@ def check_routing(f, ref):
     check_gates(host(f.topk_w), ref["topk_w"])
 
 
-@pytest.mark.parametrize("name", ["tiny-f32", "mid-ragged", "mid-gshard", "mid-wide-k"])
+@pytest.mark.parametrize("name", ["tiny-f32", "mid-ragged", "mid-gshard", "mid-wide-k",
+                                  "mid-many-experts", "mid-smallm", "2b"])
 def test_route_alone(name):
     cfg, inp, ref = case(name)
     announce(f"route {name}")
