@@ -38,6 +38,8 @@
  *   - Requirements (else MOE_ERR_UNSUPPORTED): N_r <= 256, 1 <= K' <= 16,
  *     K' <= N_r; for MOE_BF16, d % 64 == 0, I % 64 == 0, I_s % 64 == 0;
  *     for MOE_F32, d % 4 == 0, I % 4 == 0, I_s % 4 == 0; T < 2^31 / 16;
+ *     every activation and weight matrix (x, x_perm, y_perm, the T*K' x I
+ *     and T x K_s*I_s intermediates, one expert's weights) below 4 GB;
  *     all pointers 16-byte aligned.  T == 0 returns MOE_OK with no work.
  */
 #ifndef MOE_H_

@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "../../include/moe.h"
 #include "kernels.h"
 
@@ -62,6 +64,15 @@ int check_layer(const moe_layer* L, int64_t T) {
   if (L->top_k < 1 || L->top_k > L->n_routed || L->top_k > 16) return MOE_ERR_INVALID_ARG;
   if (L->n_routed > 256) return MOE_ERR_UNSUPPORTED;
   if (T >= (int64_t{1} << 31) / 16) return MOE_ERR_UNSUPPORTED;
+  // Every activation and weight matrix must stay below 4 GB (32-bit byte
+  // offsets inside the GEMM kernels).
+  const int64_t e = static_cast<int64_t>(elt_bytes(L));
+  const int64_t P = T * L->top_k;
+  const int64_t wsh = static_cast<int64_t>(L->n_shared) * (L->n_shared > 0 ? L->d_ff_shared : 0);
+  const int64_t lim = int64_t{1} << 32;
+  if (P * std::max(L->d_model, L->d_ff) * e >= lim || T * wsh * e >= lim ||
+      wsh * L->d_model * e >= lim || static_cast<int64_t>(L->d_ff) * L->d_model * e >= lim)
+    return MOE_ERR_UNSUPPORTED;
   const int q = (L->dtype == MOE_BF16) ? 64 : 4;
   if (L->d_model % q != 0 || L->d_ff % q != 0) return MOE_ERR_UNSUPPORTED;
   if (L->n_shared > 0 && L->d_ff_shared % q != 0) return MOE_ERR_UNSUPPORTED;
@@ -105,6 +116,8 @@ moe::GemmArgs routed_gate_up(const moe_layer* L, int64_t T, const int32_t* offse
   g.A = A;
   g.lda = L->d_model;
   g.gather = gather;
+  g.a_bytes = (gather ? T : T * L->top_k) * static_cast<int64_t>(L->d_model) * elt_bytes(L);
+  g.b_bytes = static_cast<int64_t>(L->d_ff) * L->d_model * elt_bytes(L);
   g.B0 = w_gate;
   g.B1 = w_up;
   g.ldb = L->d_model;
@@ -128,6 +141,8 @@ moe::GemmArgs routed_down(const moe_layer* L, int64_t T, const int32_t* offsets,
   g.A = H;
   g.lda = L->d_ff;
   g.gather = nullptr;
+  g.a_bytes = T * L->top_k * static_cast<int64_t>(L->d_ff) * elt_bytes(L);
+  g.b_bytes = static_cast<int64_t>(L->d_model) * L->d_ff * elt_bytes(L);
   g.B0 = w_down;
   g.B1 = nullptr;
   g.ldb = L->d_ff;
@@ -157,6 +172,8 @@ moe::GemmArgs shared_gate_up(const moe_layer* L, int64_t T, const void* x, const
   g.rows_total = T;
   g.A = x;
   g.lda = L->d_model;
+  g.a_bytes = T * static_cast<int64_t>(L->d_model) * elt_bytes(L);
+  g.b_bytes = static_cast<int64_t>(wsh) * L->d_model * elt_bytes(L);
   g.B0 = ws_gate;
   g.B1 = ws_up;
   g.ldb = L->d_model;
@@ -179,6 +196,8 @@ moe::GemmArgs shared_down(const moe_layer* L, int64_t T, const void* h_shared,
   h.rows_total = T;
   h.A = h_shared;
   h.lda = wsh;
+  h.a_bytes = T * static_cast<int64_t>(wsh) * elt_bytes(L);
+  h.b_bytes = static_cast<int64_t>(wsh) * L->d_model * elt_bytes(L);
   h.B0 = ws_down;
   h.ldb = L->d_ff_shared;
   h.k_sub = L->d_ff_shared;

@@ -27,12 +27,22 @@ namespace {
 constexpr int BK = 64;          // bf16 elements per K step (128 B per row)
 constexpr int kChunks = BK / 8; // 16-byte chunks per row
 constexpr int kXcds = 8;
-constexpr int kMaxGroups = 256;
 
-// 16 bytes per lane from global memory straight into LDS (the 64 lanes of the
-// wavefront fill 1 KB starting at the wave-uniform address lds).
-__device__ __forceinline__ void copy_to_lds16(const bf16_t* src, bf16_t* lds) {
-  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+// Buffer resource over `bytes` bytes at `base` (raw buffer: offsets are byte
+// offsets; loads past `bytes` return zero instead of faulting).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+__device__ __forceinline__ lds_void_ptr lds_ptr(bf16_t* p) { return (lds_void_ptr)(p); }
+
+// 16 bytes per lane straight into LDS: the 64 lanes of the wavefront fill
+// the 1 KB at the wave-uniform address lds (buffer_load_dwordx4 ... lds).
+__device__ __forceinline__ void copy_to_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                              bf16_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, lds_ptr(lds), 16, voff, soff, 0, 0);
 }
 
 // silu(a) = a * sigmoid(a) with the hardware reciprocal (epilogue only).
@@ -51,10 +61,97 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return xcd * base + min(xcd, rem) + local;
 }
 
+// Asynchronous global -> LDS copy of K step kt into stage buffer s: A_LD
+// 8-row loads for A and B_LD for B per wavefront.  Per-lane byte offsets are
+// fixed over K; the K position goes in the scalar offset.
+template <int BM, int BN, int A_LD, int B_LD>
+__device__ __forceinline__ void copy_step(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                          const uint32_t (&a_off)[A_LD], const uint32_t (&b_off)[B_LD],
+                                          int kt, int k_sub, int64_t b_sub_stride, int wv, bf16_t* s) {
+  const int k = kt * BK;
+  const uint32_t sa = static_cast<uint32_t>(k) * 2u;
+  const uint32_t sb = static_cast<uint32_t>(
+      (static_cast<int64_t>(k / k_sub) * b_sub_stride + (k % k_sub)) * 2);
+#pragma unroll
+  for (int i = 0; i < A_LD; ++i) copy_to_lds16(ra, a_off[i], sa, s + (wv * A_LD + i) * 8 * BK);
+#pragma unroll
+  for (int i = 0; i < B_LD; ++i)
+    copy_to_lds16(rb, b_off[i], sb, s + BM * BK + (wv * B_LD + i) * 8 * BK);
+}
+
+// One K step: start the copy of step kn into `nxt`, then read fragments of
+// `cur` and run the MFMAs while the copy is in flight.  `cur` and `nxt` are
+// distinct stages (restrict), so no wait on the copy is needed before the
+// reads; the compiler puts it before the closing barrier.
+template <int BM, int BN, int MB, int NB, int A_LD, int B_LD>
+__device__ __forceinline__ void mma_step(f32x16 (&acc)[MB][NB], const bf16_t* __restrict__ cur,
+                                         bf16_t* __restrict__ nxt, __amdgpu_buffer_rsrc_t ra,
+                                         __amdgpu_buffer_rsrc_t rb, const uint32_t (&a_off)[A_LD],
+                                         const uint32_t (&b_off)[B_LD], int kn, int k_sub,
+                                         int64_t b_sub_stride, int wv, const int (&a_row)[MB],
+                                         const int (&b_row)[NB], int khalf) {
+  {
+    const int k = kn * BK;
+    const uint32_t sa = static_cast<uint32_t>(k) * 2u;
+    const uint32_t sb = static_cast<uint32_t>(
+        (static_cast<int64_t>(k / k_sub) * b_sub_stride + (k % k_sub)) * 2);
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, lds_ptr(nxt + (wv * A_LD + i) * 8 * BK),
+          16, a_off[i], sa, 0, 0);
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb,
+          lds_ptr(nxt + BM * BK + (wv * B_LD + i) * 8 * BK),
+          16, b_off[i], sb, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // Fragments of K slice kk+1 are read while the MFMAs of slice kk run.
+  bf16x8 af[2][MB], bfr[2][NB];
+  auto read = [&](int kk, int buf) {
+    const int c = kk * 2 + khalf;
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+      af[buf][i] = *reinterpret_cast<const bf16x8*>(cur + a_row[i] * BK + ((c ^ swz(a_row[i])) * 8));
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      bfr[buf][j] = *reinterpret_cast<const bf16x8*>(cur + BM * BK + b_row[j] * BK +
+                                                     ((c ^ swz(b_row[j])) * 8));
+  };
+  read(0, 0);
+#pragma unroll
+  for (int kk = 0; kk < BK / 16; ++kk) {
+    if (kk + 1 < BK / 16) read(kk + 1, (kk + 1) & 1);
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][i], bfr[kk & 1][j], acc[i][j],
+                                                            0, 0, 0);
+    // Interleave: the MB+NB fragment reads of the next slice between this
+    // slice's MB*NB MFMAs, so their latency hides behind the matrix cores.
+    if (kk + 1 < BK / 16) {
+#pragma unroll
+      for (int r = 0; r < MB + NB; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, (MB * NB) / (MB + NB), 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                      // LDS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, MB * NB - (MB * NB) / (MB + NB) * (MB + NB), 0);
+    }
+  }
+  // The MFMAs stay ahead of the barrier; the compiler puts the wait for the
+  // copy (vmcnt) right before it.
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+}
+
 // GROUPED: rows come in per-expert groups described by offsets (routed
 // experts); otherwise one dense group (shared experts).
 template <int BM, int BN, int WM, int WN, int MODE, bool GROUPED>
 __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr int NT = WM * WN * kWave;
   constexpr int TM = BM / WM;               // rows per wavefront
   constexpr int TN = BN / WN;               // B rows per wavefront
@@ -68,8 +165,6 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
   static_assert(MODE == kDown || NB % 2 == 0, "gate/up needs paired blocks");
 
   __shared__ __attribute__((aligned(16))) bf16_t smem[2][(BM + BN) * BK];
-  __shared__ int s_tiles[kMaxGroups + 1];
-  __shared__ int s_group, s_row0, s_rows;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -89,33 +184,39 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
     rows = static_cast<int>(min<int64_t>(BM, p.rows_total - row0));
     if (rows <= 0) return;
   } else {
+    // Each wavefront finds the group of row tile mt on its own, 64 groups at
+    // a time: per-lane tile counts, a shuffle prefix sum, and a ballot.
     const int G = p.n_groups;
-    // inclusive scan of per-group tile counts (G <= 256, NT >= 64)
-    for (int i = tid; i < G; i += NT) {
-      const int m = p.offsets[i + 1] - p.offsets[i];
-      s_tiles[i + 1] = (m + BM - 1) / BM;
-    }
-    if (tid == 0) s_tiles[0] = 0;
-    __syncthreads();
-    if (tid == 0) {
-      int run = 0;
-      int found = -1;
-      for (int i = 0; i < G; ++i) {
-        const int c = s_tiles[i + 1];
-        if (found < 0 && mt < run + c) {
-          found = i;
-          s_row0 = p.offsets[i] + (mt - run) * BM;
-          s_rows = min(BM, p.offsets[i + 1] - s_row0);
-        }
-        run += c;
+    g = -1;
+    row0 = 0;
+    rows = 0;
+    int base = 0;
+    for (int g0 = 0; g0 < G; g0 += kWave) {
+      const int gi = g0 + lane;
+      const int m = gi < G ? p.offsets[gi + 1] - p.offsets[gi] : 0;
+      const int cnt = (m + BM - 1) / BM;
+      int incl = cnt;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int v = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += v;
       }
-      s_group = found;
+      const int excl = incl - cnt;
+      const uint64_t hit = __ballot(mt >= base + excl && mt < base + incl);
+      if (hit != 0) {
+        const int src = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+        g = g0 + src;
+        const int first = base + __shfl(excl, src, kWave);
+        row0 = p.offsets[g] + (mt - first) * BM;
+        rows = min(BM, p.offsets[g + 1] - row0);
+        break;
+      }
+      base += __shfl(incl, kWave - 1, kWave);
     }
-    __syncthreads();
-    g = s_group;
+    g = __builtin_amdgcn_readfirstlane(g);
     if (g < 0) return;
-    row0 = s_row0;
-    rows = s_rows;
+    row0 = __builtin_amdgcn_readfirstlane(row0);
+    rows = __builtin_amdgcn_readfirstlane(rows);
   }
 
   const bf16_t* A = static_cast<const bf16_t*>(p.A);
@@ -132,45 +233,32 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int lr = lane >> 3;
   const int lp = lane & 7;
-  const bf16_t* a_src[A_LD];
+  // Byte offsets (32-bit: every operand matrix is below 4 GB, checked by the
+  // host) into buffer resources over A and over this wavefront's B matrix.
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, static_cast<uint32_t>(p.a_bytes));
+  uint32_t a_off[A_LD];
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
     const int r = (wv * A_LD + i) * 8 + lr;
     const int c = lp ^ swz(r);
     const int64_t grow = row0 + min(r, rows - 1);
     const int64_t arow = p.gather ? p.gather[grow] : grow;
-    a_src[i] = A + arow * p.lda + c * 8;
+    a_off[i] = static_cast<uint32_t>((arow * p.lda + c * 8) * 2);
   }
-  const bf16_t* b_src[B_LD];
+  // All B rows one wavefront copies come from the same matrix (W1 or W3 in
+  // gate/up mode: the wavefront's 8*B_LD rows never straddle the boundary).
+  const bool up = (MODE == kGateUp) && (wv * B_LD * 8 >= BN / 2);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(up ? B1 : B0, static_cast<uint32_t>(p.b_bytes));
+  uint32_t b_off[B_LD];
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) {
     const int r = (wv * B_LD + i) * 8 + lr;
     const int c = lp ^ swz(r);
-    const bf16_t* base;
-    int n;
-    if (MODE == kGateUp) {
-      const bool up = r >= BN / 2;
-      n = nt * OUT_N + (up ? r - BN / 2 : r);
-      base = up ? B1 : B0;
-    } else {
-      n = nt * OUT_N + r;
-      base = B0;
-    }
+    int n = nt * OUT_N + ((MODE == kGateUp && up) ? r - BN / 2 : r);
     n = min(n, p.N - 1);
-    b_src[i] = base + static_cast<int64_t>(n) * p.ldb + c * 8;
+    b_off[i] = static_cast<uint32_t>((static_cast<int64_t>(n) * p.ldb + c * 8) * 2);
   }
-
-  // Asynchronous global -> LDS copy of K step kt into stage buffer s.
-  auto issue = [&](int kt, bf16_t* s) {
-    const int k = kt * BK;
-    const int64_t boff = static_cast<int64_t>(k / p.k_sub) * p.b_sub_stride + (k % p.k_sub);
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i)
-      copy_to_lds16(a_src[i] + k, s + (wv * A_LD + i) * 8 * BK);
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i)
-      copy_to_lds16(b_src[i] + boff, s + BM * BK + (wv * B_LD + i) * 8 * BK);
-  };
+  static_assert(MODE == kDown || (BN / 2) % (8 * B_LD) == 0, "B rows of a wavefront straddle W1/W3");
 
   f32x16 acc[MB][NB];
 #pragma unroll
@@ -197,46 +285,19 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
     }
   }
 
-  // Per K step: read every fragment of the current stage into registers,
-  // then start the asynchronous copy of the next step into the other stage
-  // (issued after the reads, so no wait on the copy is needed before them),
-  // then run the step's MFMAs while the copy is in flight.
+  // Two-stage pipeline: each step first starts the asynchronous copy of the
+  // next K step into the other stage, then runs this step's MFMAs on the
+  // current stage, then waits for the copy.  The copy of the last step is
+  // repeated in bounds so the step body has no branch.
   const int nk = p.K / BK;
-  issue(0, smem[0]);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  const int64_t kstride_b = p.b_sub_stride;
+  copy_step<BM, BN, A_LD, B_LD>(ra, rb, a_off, b_off, 0, p.k_sub, kstride_b, wv, smem[0]);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int stage = kt & 1;
-    const bf16_t* s = smem[stage];
-    bf16x8 af[BK / 16][MB], bfr[BK / 16][NB];
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int c = kk * 2 + khalf;
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-        af[kk][i] = *reinterpret_cast<const bf16x8*>(s + a_row[i] * BK + ((c ^ swz(a_row[i])) * 8));
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-        bfr[kk][j] = *reinterpret_cast<const bf16x8*>(s + BM * BK + b_row[j] * BK +
-                                                      ((c ^ swz(b_row[j])) * 8));
-      // keep the reads in K order so each slice's MFMAs wait only for it
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // Unconditional (the last step re-copies itself, in bounds) so no branch
-    // sits between the fragment reads and the MFMAs that wait on them.
-    issue(min(kt + 1, nk - 1), smem[stage ^ 1]);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk)
-#pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk][i], bfr[kk][j], acc[i][j], 0, 0, 0);
-    // the MFMAs stay ahead of the wait for the copy
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    mma_step<BM, BN, MB, NB, A_LD, B_LD>(acc, smem[stage], smem[stage ^ 1], ra, rb, a_off, b_off,
+                                         min(kt + 1, nk - 1), p.k_sub, kstride_b, wv, a_row, b_row,
+                                         khalf);
   }
 
   // ---- epilogue: D[row][col] of a 32x32 block sits in lane (col + 32*h),
@@ -277,6 +338,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
       }
     }
   }
+#endif
 }
 
 template <int BM, int BN, int WM, int WN>
@@ -311,7 +373,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.rows_total == 0) return hipSuccess;
   const int64_t mean_rows = a.rows_total / (a.offsets ? a.n_groups : 1);
-  if (mean_rows >= 192) return launch_cfg<256, 256, 2, 2>(a, s);
+  if (mean_rows >= 192) return launch_cfg<256, 256, 2, 4>(a, s);
   if (mean_rows >= 64) return launch_cfg<128, 256, 2, 2>(a, s);
   return launch_cfg<32, 256, 1, 4>(a, s);
 }

@@ -45,6 +45,8 @@ enum GemmMode { kGateUp = 0, kDown = 1 };
 // kGateUp: C[r, n] = silu(A_r . B0_n) * (A_r . B1_n), n < N.
 // kDown:   C[r, n] = A_r . B0_n.
 struct GemmArgs {
+  int64_t a_bytes;         // bytes of A readable through row indices (< 4 GB)
+  int64_t b_bytes;         // bytes of one group's B0 (and of its B1) (< 4 GB)
   const int32_t* offsets;
   int n_groups;
   int64_t rows_total;      // sum of group rows (host known: P or T)
