@@ -172,21 +172,44 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
   const int wm = wave / WN, wn = wave % WN;
 
   const int n_ntiles = (p.N + OUT_N - 1) / OUT_N;
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int mt = bid / n_ntiles;
-  const int nt = bid % n_ntiles;
 
-  // ---- locate (group, first row, rows) of row tile mt ------------------
-  int g, row0, rows;
+  // ---- locate (group, first row, rows) of this workgroup's tile ---------
+  // Tiles are ordered row tile major (the n_ntiles column tiles of one row
+  // tile are consecutive), and consecutive tiles go to the same XCD so they
+  // share its L2: the remap spreads the real tiles evenly over the XCDs.
+  int g, row0, rows, mt, nt;
   if (!GROUPED) {
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    mt = bid / n_ntiles;
+    nt = bid % n_ntiles;
     g = 0;
     row0 = mt * BM;
     rows = static_cast<int>(min<int64_t>(BM, p.rows_total - row0));
     if (rows <= 0) return;
   } else {
-    // Each wavefront finds the group of row tile mt on its own, 64 groups at
-    // a time: per-lane tile counts, a shuffle prefix sum, and a ballot.
+    // Row tiles per group are known only on the device.  Each wavefront
+    // scans the groups 64 at a time (per-lane tile counts, shuffle prefix
+    // sums, ballot) - first for the total, then for the group of its tile.
     const int G = p.n_groups;
+    int total = 0;
+    for (int g0 = 0; g0 < G; g0 += kWave) {
+      const int gi = g0 + lane;
+      const int m = gi < G ? p.offsets[gi + 1] - p.offsets[gi] : 0;
+      int c = (m + BM - 1) / BM;
+#pragma unroll
+      for (int o = kWave / 2; o > 0; o >>= 1) c += __shfl_xor(c, o, kWave);
+      total += c;
+    }
+    total = __builtin_amdgcn_readfirstlane(total);
+    const int real = total * n_ntiles;
+    // XCD x owns the contiguous range of real tiles [x*real/8, (x+1)*real/8)
+    const int xcd = blockIdx.x % kXcds;
+    const int local = blockIdx.x / kXcds;
+    const int base_n = real / kXcds, rem = real % kXcds;
+    if (local >= base_n + (xcd < rem ? 1 : 0)) return;
+    const int bid = xcd * base_n + min(xcd, rem) + local;
+    mt = bid / n_ntiles;
+    nt = bid % n_ntiles;
     g = -1;
     row0 = 0;
     rows = 0;
