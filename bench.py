@@ -31,10 +31,11 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
-# rocprofv3 FETCH_SIZE / WRITE_SIZE of the routed gate/up kernel on this workload,
-# already divided by the copy-kernel calibration factor; None until measured
-# for the current kernel.
-TRAFFIC_BYTES = None
+# HBM bytes per launch of the routed gate/up kernel on the 16b layer, from
+# rocprofv3 FETCH_SIZE (x2) and WRITE_SIZE (x1) in KiB, the factors taken from
+# a plain 1 GiB copy in the same run (profiles/grouped_gemm_gate_up_16b_fetch_write.md).
+# None whenever the kernel has changed since the counters were taken.
+TRAFFIC_BYTES = {"16b": (1810930 * 2 + 270336) * 1024}
 
 
 def parse():
@@ -211,7 +212,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": gu_tflops / PEAK_BF16_TFLOPS,
-            "traffic": TRAFFIC_BYTES,
+            "traffic": TRAFFIC_BYTES.get(cfg.name),
             "algorithmic_flop_per_launch": gu_flop,
             "avg_launch_ms": gu_ms,
         },
