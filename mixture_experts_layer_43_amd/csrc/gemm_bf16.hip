@@ -24,8 +24,6 @@ namespace moe {
 
 namespace {
 
-constexpr int BK = 64;          // bf16 elements per K step (128 B per row)
-constexpr int kChunks = BK / 8; // 16-byte chunks per row
 constexpr int kXcds = 8;
 
 // Buffer resource over `bytes` bytes at `base` (raw buffer: offsets are byte
@@ -37,21 +35,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 __device__ __forceinline__ lds_void_ptr lds_ptr(bf16_t* p) { return (lds_void_ptr)(p); }
 
-// 16 bytes per lane straight into LDS: the 64 lanes of the wavefront fill
-// the 1 KB at the wave-uniform address lds (buffer_load_dwordx4 ... lds).
-__device__ __forceinline__ void copy_to_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
-                                              bf16_t* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      r, lds_ptr(lds), 16, voff, soff, 0, 0);
-}
-
 // silu(a) = a * sigmoid(a) with the hardware reciprocal (epilogue only).
 __device__ __forceinline__ float silu_fast(float a) {
   return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a));
 }
 
-// 16-byte chunk c of tile row r is stored at chunk position c ^ swz(r).
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// A tile row holds BK bf16 = BK/8 16-byte chunks; chunk c of row r is stored
+// at chunk position c ^ swz(r).  Both patterns keep the 16-byte fragment
+// reads of any 8 (and any 16) consecutive rows on distinct LDS banks.
+template <int BK>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (BK == 64) return (r & 7) ^ ((r >> 3) & 1);
+  else return ((r >> 1) ^ (r >> 3)) & 3;
+}
 
 __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   const int xcd = bid % kXcds;
@@ -61,110 +57,184 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return xcd * base + min(xcd, rem) + local;
 }
 
-// Asynchronous global -> LDS copy of K step kt into stage buffer s: A_LD
-// 8-row loads for A and B_LD for B per wavefront.  Per-lane byte offsets are
-// fixed over K; the K position goes in the scalar offset.
-template <int BM, int BN, int A_LD, int B_LD>
+// s_waitcnt with vmcnt <= N (gfx9 encoding: vmcnt in bits 3:0 and 15:14;
+// expcnt and lgkmcnt at their maxima, i.e. not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Wait until at most `ahead` K steps of this wavefront's copies (L loads per
+// step) are still in flight; `ahead` is wave-uniform and below STAGES-1.
+template <int L, int STAGES>
+__device__ __forceinline__ void wait_steps(int ahead) {
+  if constexpr (STAGES >= 4) {
+    if (ahead >= 2) { wait_vmcnt<2 * L>(); return; }
+  }
+  if constexpr (STAGES >= 3) {
+    if (ahead >= 1) { wait_vmcnt<L>(); return; }
+  }
+  wait_vmcnt<0>();
+}
+
+// Workgroup barrier with no memory fence: the copies into LDS are waited for
+// explicitly (wait_steps) so that the ones for later K steps stay in flight.
+// The empty asm keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Asynchronous global -> LDS copy of the K step starting at element k into
+// stage `s`: A_LD loads for A rows and B_LD for B rows per wavefront, each
+// 64 lanes x 16 B = 1 KB of LDS (64/(BK/8) tile rows).  Per-lane byte
+// offsets are fixed over K; the K position goes in the scalar offset.
+template <int BM, int BK, int A_LD, int B_LD>
 __device__ __forceinline__ void copy_step(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                           const uint32_t (&a_off)[A_LD], const uint32_t (&b_off)[B_LD],
-                                          int kt, int k_sub, int64_t b_sub_stride, int wv, bf16_t* s) {
-  const int k = kt * BK;
+                                          int k, int k_sub, int64_t b_sub_stride, int wv,
+                                          bf16_t* __restrict__ s) {
+  constexpr int R = kWave / (BK / 8);
   const uint32_t sa = static_cast<uint32_t>(k) * 2u;
   const uint32_t sb = static_cast<uint32_t>(
       (static_cast<int64_t>(k / k_sub) * b_sub_stride + (k % k_sub)) * 2);
 #pragma unroll
-  for (int i = 0; i < A_LD; ++i) copy_to_lds16(ra, a_off[i], sa, s + (wv * A_LD + i) * 8 * BK);
+  for (int i = 0; i < A_LD; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds_ptr(s + (wv * A_LD + i) * R * BK), 16, a_off[i],
+                                             sa, 0, 0);
 #pragma unroll
   for (int i = 0; i < B_LD; ++i)
-    copy_to_lds16(rb, b_off[i], sb, s + BM * BK + (wv * B_LD + i) * 8 * BK);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, lds_ptr(s + BM * BK + (wv * B_LD + i) * R * BK), 16,
+                                             b_off[i], sb, 0, 0);
 }
 
-// One K step: start the copy of step kn into `nxt`, then read fragments of
-// `cur` and run the MFMAs while the copy is in flight.  `cur` and `nxt` are
-// distinct stages (restrict), so no wait on the copy is needed before the
-// reads; the compiler puts it before the closing barrier.
-template <int BM, int BN, int MB, int NB, int A_LD, int B_LD>
-__device__ __forceinline__ void mma_step(f32x16 (&acc)[MB][NB], const bf16_t* __restrict__ cur,
-                                         bf16_t* __restrict__ nxt, __amdgpu_buffer_rsrc_t ra,
-                                         __amdgpu_buffer_rsrc_t rb, const uint32_t (&a_off)[A_LD],
-                                         const uint32_t (&b_off)[B_LD], int kn, int k_sub,
-                                         int64_t b_sub_stride, int wv, const int (&a_row)[MB],
-                                         const int (&b_row)[NB], int khalf) {
-  {
-    const int k = kn * BK;
-    const uint32_t sa = static_cast<uint32_t>(k) * 2u;
-    const uint32_t sb = static_cast<uint32_t>(
-        (static_cast<int64_t>(k / k_sub) * b_sub_stride + (k % k_sub)) * 2);
+// Fragments of one 16-wide K slice: lane l holds 8 consecutive k of tile row
+// a_row/b_row (= l%32 within its 32-row block), K half l/32.  Only the
+// first MBA of the MB row blocks are read and multiplied: row blocks past
+// the last row of a partial tile are skipped.
+template <int MB, int NB>
+struct Frags {
+  bf16x8 a[2][MB], b[2][NB];
+};
+
+template <int BM, int BK, int MB, int NB, int MBA>
+__device__ __forceinline__ void read_slice(Frags<MB, NB>& f, const bf16_t* __restrict__ cur, int kk,
+                                           int buf, int khalf, const int (&a_row)[MB],
+                                           const int (&b_row)[NB]) {
+  const int c = kk * 2 + khalf;
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, lds_ptr(nxt + (wv * A_LD + i) * 8 * BK),
-          16, a_off[i], sa, 0, 0);
+  for (int i = 0; i < MBA; ++i)
+    f.a[buf][i] = *reinterpret_cast<const bf16x8*>(cur + a_row[i] * BK + ((c ^ swz<BK>(a_row[i])) * 8));
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rb,
-          lds_ptr(nxt + BM * BK + (wv * B_LD + i) * 8 * BK),
-          16, b_off[i], sb, 0, 0);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  // Fragments of K slice kk+1 are read while the MFMAs of slice kk run.
-  bf16x8 af[2][MB], bfr[2][NB];
-  auto read = [&](int kk, int buf) {
-    const int c = kk * 2 + khalf;
+  for (int j = 0; j < NB; ++j)
+    f.b[buf][j] =
+        *reinterpret_cast<const bf16x8*>(cur + BM * BK + b_row[j] * BK + ((c ^ swz<BK>(b_row[j])) * 8));
+}
+
+template <int MB, int NB, int MBA>
+__device__ __forceinline__ void mma_slice(f32x16 (&acc)[MB][NB], const Frags<MB, NB>& f, int buf) {
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
-      af[buf][i] = *reinterpret_cast<const bf16x8*>(cur + a_row[i] * BK + ((c ^ swz(a_row[i])) * 8));
+  for (int i = 0; i < MBA; ++i)
 #pragma unroll
     for (int j = 0; j < NB; ++j)
-      bfr[buf][j] = *reinterpret_cast<const bf16x8*>(cur + BM * BK + b_row[j] * BK +
-                                                     ((c ^ swz(b_row[j])) * 8));
-  };
-  read(0, 0);
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[buf][i], f.b[buf][j], acc[i][j], 0, 0, 0);
+}
+
+// Scheduling pattern for one slice's MBA*NB MFMAs with the MBA+NB fragment
+// reads of the next slice spread between them.
+template <int MBA, int NB>
+__device__ __forceinline__ void interleave() {
+  constexpr int per = (MBA * NB) / (MBA + NB);
 #pragma unroll
-  for (int kk = 0; kk < BK / 16; ++kk) {
-    if (kk + 1 < BK / 16) read(kk + 1, (kk + 1) & 1);
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][i], bfr[kk & 1][j], acc[i][j],
-                                                            0, 0, 0);
-    // Interleave: the MB+NB fragment reads of the next slice between this
-    // slice's MB*NB MFMAs, so their latency hides behind the matrix cores.
-    if (kk + 1 < BK / 16) {
-#pragma unroll
-      for (int r = 0; r < MB + NB; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x008, (MB * NB) / (MB + NB), 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                      // LDS read
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, MB * NB - (MB * NB) / (MB + NB) * (MB + NB), 0);
-    }
+  for (int r = 0; r < MBA + NB; ++r) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // LDS read
+    __builtin_amdgcn_sched_group_barrier(0x008, per, 0);  // MFMA
   }
-  // The MFMAs stay ahead of the barrier; the compiler puts the wait for the
-  // copy (vmcnt) right before it.
+  __builtin_amdgcn_sched_group_barrier(0x008, MBA * NB - per * (MBA + NB), 0);
   __builtin_amdgcn_sched_barrier(0);
-  __syncthreads();
+}
+
+// One K step on stage `cur`, with the copy of a later step into the other
+// stages already issued.  The MFMAs of the previous step's last slice
+// (register buffer 1, read before the barrier) run while slice 0 of this
+// step is read, so the matrix cores have work across the barrier.  The last
+// slice of this step is only read here; its MFMAs run in the next step (or
+// after the loop).
+template <int BM, int BK, int MB, int NB, int MBA>
+__device__ __forceinline__ void step_body(f32x16 (&acc)[MB][NB], Frags<MB, NB>& f,
+                                          const bf16_t* __restrict__ cur, bool has_prev, int khalf,
+                                          const int (&a_row)[MB], const int (&b_row)[NB]) {
+  constexpr int NS = BK / 16;
+  read_slice<BM, BK, MB, NB, MBA>(f, cur, 0, 0, khalf, a_row, b_row);
+  if (has_prev) {
+    mma_slice<MB, NB, MBA>(acc, f, 1);
+    interleave<MBA, NB>();
+  } else {
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int kk = 0; kk + 1 < NS; ++kk) {
+    read_slice<BM, BK, MB, NB, MBA>(f, cur, kk + 1, (kk + 1) & 1, khalf, a_row, b_row);
+    mma_slice<MB, NB, MBA>(acc, f, kk & 1);
+    interleave<MBA, NB>();
+  }
+}
+
+// The STAGES-deep K loop.  The copies of the first STAGES-1 K steps were
+// issued by the caller.  Step kt waits for its own copy (leaving the later
+// ones in flight), meets the other wavefronts at a barrier (after which
+// every copy of step kt has landed and nobody reads stage (kt-1) % STAGES
+// any more), issues the copy of step kt+STAGES-1 into that stage and
+// computes.  A wavefront whose rows are all past the tile's last row
+// (MBA == 0) only copies and waits.
+template <int BM, int BK, int STAGES, int MB, int NB, int MBA, int A_LD, int B_LD>
+__device__ __forceinline__ void k_loop(f32x16 (&acc)[MB][NB], __amdgpu_buffer_rsrc_t ra,
+                                       __amdgpu_buffer_rsrc_t rb, const uint32_t (&a_off)[A_LD],
+                                       const uint32_t (&b_off)[B_LD], int nk, int k_sub,
+                                       int64_t kstride_b, int wv, int khalf, const int (&a_row)[MB],
+                                       const int (&b_row)[NB], bf16_t* smem, int se) {
+  constexpr int L = A_LD + B_LD;
+  Frags<MB, NB> fr;
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_steps<L, STAGES>(min(STAGES - 2, nk - 1 - kt));
+    lds_barrier();
+    const int kn = kt + STAGES - 1;
+    if (kn < nk)
+      copy_step<BM, BK, A_LD, B_LD>(ra, rb, a_off, b_off, kn * BK, k_sub, kstride_b, wv,
+                                    smem + (kn % STAGES) * se);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (MBA > 0)
+      step_body<BM, BK, MB, NB, MBA>(acc, fr, smem + (kt % STAGES) * se, kt > 0, khalf, a_row, b_row);
+  }
+  if constexpr (MBA > 0) mma_slice<MB, NB, MBA>(acc, fr, 1);
 }
 
 // GROUPED: rows come in per-expert groups described by offsets (routed
 // experts); otherwise one dense group (shared experts).
-template <int BM, int BN, int WM, int WN, int MODE, bool GROUPED>
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int MODE, bool GROUPED>
 __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
-  constexpr int NT = WM * WN * kWave;
   constexpr int TM = BM / WM;               // rows per wavefront
   constexpr int TN = BN / WN;               // B rows per wavefront
   constexpr int MB = TM / 32;
   constexpr int NB = TN / 32;
   constexpr int OUT_N = (MODE == kGateUp) ? BN / 2 : BN;
   constexpr int NW = WM * WN;
-  constexpr int A_LD = BM / 8 / NW;         // 8-row LDS loads per wavefront per K step
-  constexpr int B_LD = BN / 8 / NW;
-  static_assert(A_LD * 8 * NW == BM && B_LD * 8 * NW == BN, "tile/wave mismatch");
+  constexpr int RPL = kWave / (BK / 8);     // tile rows per 1 KB LDS load
+  constexpr int A_LD = BM / RPL / NW;       // loads per wavefront per K step
+  constexpr int B_LD = BN / RPL / NW;
+  constexpr int SE = (BM + BN) * BK;        // elements per stage
+  static_assert(BK == 32 || BK == 64, "K step");
+  static_assert(STAGES >= 2 && STAGES <= 4, "stages");
+  static_assert(A_LD * RPL * NW == BM && B_LD * RPL * NW == BN, "tile/wave mismatch");
   static_assert(MODE == kDown || NB % 2 == 0, "gate/up needs paired blocks");
+  static_assert((BK / 16) % 2 == 0, "slices alternate register buffers");
 
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2][(BM + BN) * BK];
+  __shared__ __attribute__((aligned(16))) bf16_t smem[STAGES * SE];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -249,39 +319,39 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
                          : nullptr;
 
   // ---- per-lane source chunks (fixed over K) -----------------------------
-  // One global_load_lds_dwordx4 moves 64 lanes x 16 B into a contiguous 1 KB
-  // of LDS: 8 tile rows of one K step.  Lane L lands on row L/8, chunk
-  // position L%8, so it fetches logical chunk (L%8) ^ swz(row): the load
+  // One load moves 64 lanes x 16 B into a contiguous 1 KB of LDS: RPL tile
+  // rows of one K step.  Lane L lands on row L/(BK/8), chunk position
+  // L%(BK/8), so it fetches logical chunk (L%(BK/8)) ^ swz(row): the load
   // itself writes the swizzled layout.
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int lr = lane >> 3;
-  const int lp = lane & 7;
+  const int lr = lane / (BK / 8);
+  const int lp = lane % (BK / 8);
   // Byte offsets (32-bit: every operand matrix is below 4 GB, checked by the
   // host) into buffer resources over A and over this wavefront's B matrix.
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, static_cast<uint32_t>(p.a_bytes));
   uint32_t a_off[A_LD];
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
-    const int r = (wv * A_LD + i) * 8 + lr;
-    const int c = lp ^ swz(r);
+    const int r = (wv * A_LD + i) * RPL + lr;
+    const int c = lp ^ swz<BK>(r);
     const int64_t grow = row0 + min(r, rows - 1);
     const int64_t arow = p.gather ? p.gather[grow] : grow;
     a_off[i] = static_cast<uint32_t>((arow * p.lda + c * 8) * 2);
   }
   // All B rows one wavefront copies come from the same matrix (W1 or W3 in
-  // gate/up mode: the wavefront's 8*B_LD rows never straddle the boundary).
-  const bool up = (MODE == kGateUp) && (wv * B_LD * 8 >= BN / 2);
+  // gate/up mode: the wavefront's RPL*B_LD rows never straddle the boundary).
+  const bool up = (MODE == kGateUp) && (wv * B_LD * RPL >= BN / 2);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(up ? B1 : B0, static_cast<uint32_t>(p.b_bytes));
   uint32_t b_off[B_LD];
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) {
-    const int r = (wv * B_LD + i) * 8 + lr;
-    const int c = lp ^ swz(r);
+    const int r = (wv * B_LD + i) * RPL + lr;
+    const int c = lp ^ swz<BK>(r);
     int n = nt * OUT_N + ((MODE == kGateUp && up) ? r - BN / 2 : r);
     n = min(n, p.N - 1);
     b_off[i] = static_cast<uint32_t>((static_cast<int64_t>(n) * p.ldb + c * 8) * 2);
   }
-  static_assert(MODE == kDown || (BN / 2) % (8 * B_LD) == 0, "B rows of a wavefront straddle W1/W3");
+  static_assert(MODE == kDown || (BN / 2) % (RPL * B_LD) == 0, "B rows of a wavefront straddle W1/W3");
 
   f32x16 acc[MB][NB];
 #pragma unroll
@@ -308,20 +378,29 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
     }
   }
 
-  // Two-stage pipeline: each step first starts the asynchronous copy of the
-  // next K step into the other stage, then runs this step's MFMAs on the
-  // current stage, then waits for the copy.  The copy of the last step is
-  // repeated in bounds so the step body has no branch.
+  // ---- K loop -------------------------------------------------------------
   const int nk = p.K / BK;
   const int64_t kstride_b = p.b_sub_stride;
-  copy_step<BM, BN, A_LD, B_LD>(ra, rb, a_off, b_off, 0, p.k_sub, kstride_b, wv, smem[0]);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int stage = kt & 1;
-    mma_step<BM, BN, MB, NB, A_LD, B_LD>(acc, smem[stage], smem[stage ^ 1], ra, rb, a_off, b_off,
-                                         min(kt + 1, nk - 1), p.k_sub, kstride_b, wv, a_row, b_row,
-                                         khalf);
+#pragma unroll
+  for (int j = 0; j < STAGES - 1; ++j)
+    if (j < nk) copy_step<BM, BK, A_LD, B_LD>(ra, rb, a_off, b_off, j * BK, p.k_sub, kstride_b, wv,
+                                               smem + j * SE);
+  // 32-row blocks of this wavefront that hold rows of the tile.
+  const int mba = __builtin_amdgcn_readfirstlane(max(0, min(MB, (rows - wm * TM + 31) / 32)));
+#define MOE_K_LOOP(n)                                                                            \
+  k_loop<BM, BK, STAGES, MB, NB, n, A_LD, B_LD>(acc, ra, rb, a_off, b_off, nk, p.k_sub, kstride_b, \
+                                                wv, khalf, a_row, b_row, smem, SE)
+  if (mba == MB) {
+    MOE_K_LOOP(MB);
+  } else if (mba == 0) {
+    MOE_K_LOOP(0);
+  } else {
+    if constexpr (MB > 1) if (mba == 1) MOE_K_LOOP(1);
+    if constexpr (MB > 2) if (mba == 2) MOE_K_LOOP(2);
+    if constexpr (MB > 3) if (mba == 3) MOE_K_LOOP(3);
+    static_assert(MB <= 4, "row blocks per wavefront");
   }
+#undef MOE_K_LOOP
 
   // ---- epilogue: D[row][col] of a 32x32 block sits in lane (col + 32*h),
   //      register v, row = 8*(v/4) + 4*h + v%4.
@@ -364,7 +443,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
 #endif
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int BK, int STAGES>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   constexpr int OUT_N = BN / 2;
   const int out_n = (a.mode == kGateUp) ? OUT_N : BN;
@@ -381,13 +460,13 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   const dim3 block(WM * WN * kWave);
   const bool grouped = a.offsets != nullptr;
   if (a.mode == kGateUp && grouped)
-    hipLaunchKernelGGL((grouped_gemm_bf16<BM, BN, WM, WN, kGateUp, true>), dim3(grid), block, 0, s, a);
+    hipLaunchKernelGGL((grouped_gemm_bf16<BM, BN, WM, WN, BK, STAGES, kGateUp, true>), dim3(grid), block, 0, s, a);
   else if (a.mode == kGateUp)
-    hipLaunchKernelGGL((grouped_gemm_bf16<BM, BN, WM, WN, kGateUp, false>), dim3(grid), block, 0, s, a);
+    hipLaunchKernelGGL((grouped_gemm_bf16<BM, BN, WM, WN, BK, STAGES, kGateUp, false>), dim3(grid), block, 0, s, a);
   else if (grouped)
-    hipLaunchKernelGGL((grouped_gemm_bf16<BM, BN, WM, WN, kDown, true>), dim3(grid), block, 0, s, a);
+    hipLaunchKernelGGL((grouped_gemm_bf16<BM, BN, WM, WN, BK, STAGES, kDown, true>), dim3(grid), block, 0, s, a);
   else
-    hipLaunchKernelGGL((grouped_gemm_bf16<BM, BN, WM, WN, kDown, false>), dim3(grid), block, 0, s, a);
+    hipLaunchKernelGGL((grouped_gemm_bf16<BM, BN, WM, WN, BK, STAGES, kDown, false>), dim3(grid), block, 0, s, a);
   return hipGetLastError();
 }
 
@@ -396,9 +475,9 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.rows_total == 0) return hipSuccess;
   const int64_t mean_rows = a.rows_total / (a.offsets ? a.n_groups : 1);
-  if (mean_rows >= 192) return launch_cfg<256, 256, 2, 4>(a, s);
-  if (mean_rows >= 64) return launch_cfg<128, 256, 2, 2>(a, s);
-  return launch_cfg<32, 256, 1, 4>(a, s);
+  if (mean_rows >= 192) return launch_cfg<256, 256, 2, 4, 64, 2>(a, s);
+  if (mean_rows >= 64) return launch_cfg<128, 256, 2, 2, 64, 2>(a, s);
+  return launch_cfg<32, 256, 1, 4, 64, 2>(a, s);
 }
 
 }  // namespace moe

@@ -200,31 +200,31 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t first, uint32_t second) {
   return __builtin_amdgcn_perm(second, first, 0x07060302u);
 }
 
-template <int MBLK, int NBLK>
-struct RouterFrag {
-  bf16x8 a[MBLK];        // x: 8 consecutive k of one token row
-  float4 w[NBLK][2];     // W_g: 8 consecutive k of one expert row
-};
+constexpr int kRW = 8;   // wavefronts per matrix-core router workgroup
 
-template <int MBLK, int NBLK>
-__device__ __forceinline__ void router_load(RouterFrag<MBLK, NBLK>& f, const bf16_t* const (&ap)[MBLK],
-                                            const float* const (&bp)[NBLK], int off) {
-#pragma unroll
-  for (int mb = 0; mb < MBLK; ++mb) f.a[mb] = *reinterpret_cast<const bf16x8*>(ap[mb] + off);
+// W_g values for one 16-wide K slice: lane l holds 8 consecutive k of
+// expert row nb*32 + l%32.
+template <int NBLK>
+__device__ __forceinline__ void load_w_slice(float4 (&w)[NBLK][2], const float* const (&wp)[NBLK],
+                                             int off) {
 #pragma unroll
   for (int nb = 0; nb < NBLK; ++nb) {
-    f.w[nb][0] = *reinterpret_cast<const float4*>(bp[nb] + off);
-    f.w[nb][1] = *reinterpret_cast<const float4*>(bp[nb] + off + 4);
+    w[nb][0] = *reinterpret_cast<const float4*>(wp[nb] + off);
+    w[nb][1] = *reinterpret_cast<const float4*>(wp[nb] + off + 4);
   }
 }
 
+// acc[mb][nb] += x_slice[mb] . (hi + mid + lo)(W_g slice nb)^T, smallest
+// part first.  One split of W_g serves all MBLK token blocks, and
+// consecutive MFMAs go to different accumulators.
 template <int MBLK, int NBLK>
-__device__ __forceinline__ void router_mma(f32x16 (&acc)[MBLK][NBLK], const RouterFrag<MBLK, NBLK>& f,
-                                           const bool (&ev)[NBLK]) {
+__device__ __forceinline__ void router_mma(f32x16 (&acc)[MBLK][NBLK], const bf16x8 (&a)[MBLK],
+                                           const float4 (&w)[NBLK][2], const bool (&ev)[NBLK]) {
+  bf16x8 bp[NBLK][3];
 #pragma unroll
   for (int nb = 0; nb < NBLK; ++nb) {
-    const float v[8] = {f.w[nb][0].x, f.w[nb][0].y, f.w[nb][0].z, f.w[nb][0].w,
-                        f.w[nb][1].x, f.w[nb][1].y, f.w[nb][1].z, f.w[nb][1].w};
+    const float v[8] = {w[nb][0].x, w[nb][0].y, w[nb][0].z, w[nb][0].w,
+                        w[nb][1].x, w[nb][1].y, w[nb][1].z, w[nb][1].w};
     uint32_t h[8], m[8], l[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) split3(ev[nb] ? v[i] : 0.0f, h[i], m[i], l[i]);
@@ -236,56 +236,62 @@ __device__ __forceinline__ void router_mma(f32x16 (&acc)[MBLK][NBLK], const Rout
       pm[i] = pack_hi(m[2 * i], m[2 * i + 1]);
       pl[i] = pack_hi(l[2 * i], l[2 * i + 1]);
     }
-    const bf16x8 bh = __builtin_bit_cast(bf16x8, ph);
-    const bf16x8 bm = __builtin_bit_cast(bf16x8, pm);
-    const bf16x8 bl = __builtin_bit_cast(bf16x8, pl);
-#pragma unroll
-    for (int mb = 0; mb < MBLK; ++mb) {
-      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mb], bl, acc[mb][nb], 0, 0, 0);
-      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mb], bm, acc[mb][nb], 0, 0, 0);
-      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mb], bh, acc[mb][nb], 0, 0, 0);
-    }
+    bp[nb][0] = __builtin_bit_cast(bf16x8, pl);
+    bp[nb][1] = __builtin_bit_cast(bf16x8, pm);
+    bp[nb][2] = __builtin_bit_cast(bf16x8, ph);
   }
+#pragma unroll
+  for (int q = 0; q < 3; ++q)
+#pragma unroll
+    for (int mb = 0; mb < MBLK; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NBLK; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], bp[nb][q], acc[mb][nb], 0, 0, 0);
 }
 
-// One workgroup: 32*MBLK tokens x 32*NBLK experts.  Wavefront w takes the
-// 16-wide K slice w of every 64-wide chunk of d (so each x and W_g element is
-// read once per workgroup), register double-buffered; the four partial
-// logit tiles are summed in LDS in wavefront order (deterministic), then
-// every wavefront selects for its share of the tokens.
+// One workgroup: 32*MBLK tokens x 32*NBLK experts, kRW wavefronts.  The
+// d/16 K slices are cut into kRW contiguous ranges, one per wavefront.  A
+// wavefront loads the x fragments of RS slices at once (one trip to HBM
+// per round) and streams W_g, which every workgroup reads and so stays in
+// L2, through a ring of RD slices in registers; each W_g value is split
+// once for all MBLK token blocks.  The partial logit tiles are summed in
+// LDS in wavefront order (deterministic), then each wavefront selects for
+// four tokens at a time.
 template <int MBLK, int NBLK>
-__global__ __launch_bounds__(kRouterThreads) void router_mfma_kernel(
+__global__ __launch_bounds__(kRW * kWave) void router_mfma_kernel(
     const bf16_t* __restrict__ x, const float* __restrict__ wg, const float* __restrict__ bias,
     int T, int d, int Nr, int K, int gate, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w) {
   constexpr int TB = 32 * MBLK;
   constexpr int NPAD = 32 * NBLK;
-  constexpr int NP = NPAD < kWave ? NPAD : kWave;
+  // Selection: groups of 16 lanes, one token each (4-step reductions).
+  constexpr int NP = 16;
   constexpr int EPL = NPAD / NP;
   constexpr int G = kWave / NP;
-  constexpr int NW = kRouterThreads / kWave;
-  static_assert((TB / NW) % G == 0, "token split");
+  constexpr int RS = 16 / MBLK;               // x slices per round
+  constexpr int RD = (MBLK * NBLK <= 2) ? 4 : 2;  // W_g slices in flight
+  static_assert((TB / kRW) % G == 0, "token split");
   __shared__ float lg[TB][NPAD + 1];
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * TB;
   const int lr = lane & 31;
-  const int kw = wave * 16 + (lane >> 5) * 8;
+  const int kh = (lane >> 5) * 8;
 
-  const bf16_t* ap[MBLK];
+  const bf16_t* xp[MBLK];
 #pragma unroll
   for (int mb = 0; mb < MBLK; ++mb) {
-    const int64_t t = min<int64_t>(tok0 + mb * 32 + lr, T - 1);
-    ap[mb] = x + t * d + kw;
+    const int64_t t = tok0 + mb * 32 + lr;
+    xp[mb] = x + (t < T ? t : static_cast<int64_t>(T) - 1) * d + kh;
   }
-  const float* bp[NBLK];
+  const float* wp[NBLK];
   bool ev[NBLK];
 #pragma unroll
   for (int nb = 0; nb < NBLK; ++nb) {
     const int e = nb * 32 + lr;
     ev[nb] = e < Nr;
-    bp[nb] = wg + static_cast<int64_t>(min(e, Nr - 1)) * d + kw;
+    wp[nb] = wg + static_cast<int64_t>(min(e, Nr - 1)) * d + kh;
   }
 
   f32x16 acc[MBLK][NBLK];
@@ -296,19 +302,38 @@ __global__ __launch_bounds__(kRouterThreads) void router_mfma_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.0f;
 
-  const int nch = d / 64;
-  RouterFrag<MBLK, NBLK> f0, f1;
-  router_load(f0, ap, bp, 0);
-  for (int c = 0; c < nch; c += 2) {
-    if (c + 1 < nch) router_load(f1, ap, bp, (c + 1) * 64);
-    router_mma(acc, f0, ev);
-    if (c + 1 >= nch) break;
-    if (c + 2 < nch) router_load(f0, ap, bp, (c + 2) * 64);
-    router_mma(acc, f1, ev);
+  const int S = d / 16;
+  const int s0 = wave * S / kRW, s1 = (wave + 1) * S / kRW;
+  // Branch-free rounds (so every wait on a load is an exact count): slices
+  // past the end of the range re-read the last slice and multiply zeros.
+  for (int rs = s0; rs < s1; rs += RS) {
+    const int last = min(RS, s1 - rs) - 1;
+    bf16x8 xa[RS][MBLK];
+#pragma unroll
+    for (int i = 0; i < RS; ++i)
+#pragma unroll
+      for (int mb = 0; mb < MBLK; ++mb)
+        xa[i][mb] = *reinterpret_cast<const bf16x8*>(xp[mb] + (rs + min(i, last)) * 16);
+    float4 wr[RD][NBLK][2];
+#pragma unroll
+    for (int i = 0; i < RD; ++i) load_w_slice<NBLK>(wr[i], wp, (rs + min(i, last)) * 16);
+    // Keep every load above at the top: the scheduler would otherwise sink
+    // them next to their first use and serialise the round trips.
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < RS; ++i) {
+      if (i > last) {
+#pragma unroll
+        for (int mb = 0; mb < MBLK; ++mb) xa[i][mb] = bf16x8{};
+      }
+      router_mma<MBLK, NBLK>(acc, xa[i], wr[i % RD], ev);
+      if (i + RD < RS) load_w_slice<NBLK>(wr[i % RD], wp, (rs + min(i + RD, last)) * 16);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   // D[row][col] of a 32x32 block: lane (col + 32*h), register v, row 8*(v/4) + 4*h + v%4.
-  for (int w = 0; w < NW; ++w) {
+  for (int w = 0; w < kRW; ++w) {
     if (wave == w) {
 #pragma unroll
       for (int mb = 0; mb < MBLK; ++mb)
@@ -335,7 +360,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_mfma_kernel(
     evq[q] = e[q] < Nr;
     bq[q] = (bias != nullptr && evq[q]) ? bias[e[q]] : 0.0f;
   }
-  for (int tl = wave * (TB / NW) + grp; tl < (wave + 1) * (TB / NW); tl += G) {
+  for (int tl = wave * (TB / kRW) + grp; tl < (wave + 1) * (TB / kRW); tl += G) {
     const int64_t t = tok0 + tl;
     if (t >= T) break;  // uniform within the group
     float z[EPL];
@@ -349,7 +374,7 @@ template <int MBLK, int NBLK>
 hipError_t launch_mfma(const RouteArgs& a, hipStream_t s) {
   constexpr int TB = 32 * MBLK;
   const int grid = (a.T + TB - 1) / TB;
-  hipLaunchKernelGGL((router_mfma_kernel<MBLK, NBLK>), dim3(grid), dim3(kRouterThreads), 0, s,
+  hipLaunchKernelGGL((router_mfma_kernel<MBLK, NBLK>), dim3(grid), dim3(kRW * kWave), 0, s,
                      static_cast<const bf16_t*>(a.x), a.w_router, a.bias, a.T, a.d, a.n_routed,
                      a.top_k, a.gate, a.topk_idx, a.topk_w);
   return hipGetLastError();
@@ -371,8 +396,11 @@ hipError_t launch_x(const RouteArgs& a, hipStream_t s) {
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   if (a.x_bf16 && a.d % 64 == 0) {
-    if (a.n_routed <= 32) return launch_mfma<2, 1>(a, s);
-    if (a.n_routed <= 64) return launch_mfma<2, 2>(a, s);
+    // Two token blocks per wavefront once there are enough tokens to fill
+    // the chip with 64-token workgroups.
+    const bool wide = a.T >= 64 * 256;
+    if (a.n_routed <= 32) return wide ? launch_mfma<2, 1>(a, s) : launch_mfma<1, 1>(a, s);
+    if (a.n_routed <= 64) return wide ? launch_mfma<2, 2>(a, s) : launch_mfma<1, 2>(a, s);
     if (a.n_routed <= 128) return launch_mfma<1, 4>(a, s);
   }
   return a.x_bf16 ? launch_x<bf16_t>(a, s) : launch_x<float>(a, s);
