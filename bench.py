@@ -9,11 +9,14 @@ that are resident in HBM before timing starts.  The timed steps run through
 moe_forward_timed, which records a HIP event pair around every stage on the
 launch stream, so per-stage GPU times come from the timed region itself.
 
-Prints one JSON line.  `roofline` is for the dominant kernel, the routed
-gate/up grouped GEMM: algorithmic FLOPs 4*P*d*I per launch (P = T*K'
-assignments) over its event-timed duration, against the bf16 dense MFMA
-peak.  `cpu_baseline` times the fp64 oracle on the first --cpu-tokens tokens
-of the same workload on the host cores.
+Prints one JSON line.  `roofline` is for the dominant kernel, the gate/up
+grouped GEMM: algorithmic FLOPs 4*R*d*I per launch over its event-timed
+duration, against the bf16 dense MFMA peak.  R = T*K' routed rows, plus
+K_s*T rows when the shared experts (of the routed width) ride in the same
+launch.  `expert_gemm_tflops` counts all expert FLOPs (routed 6*T*K'*d*I
+and shared 6*T*d*K_s*I_s) over the four GEMM stages.  `cpu_baseline` times
+the fp64 oracle on the first --cpu-tokens tokens of the same workload on
+the host cores.
 """
 from __future__ import annotations
 
@@ -163,15 +166,19 @@ def main():
 
     T, dm, I, K = cfg.tokens, cfg.d_model, cfg.d_ff, cfg.top_k
     P = T * K
-    gu_flop = 4.0 * P * dm * I
-    dn_flop = 2.0 * P * dm * I
+    # With I_s == I the shared experts run as K_s extra groups of T rows in
+    # the routed gate/up and down launches (moe_forward's documented rule).
+    fold = cfg.n_shared > 0 and cfg.d_ff_shared == I
+    rows = P + (T * cfg.n_shared if fold else 0)
+    gu_flop = 4.0 * rows * dm * I            # one launch of the gate/up kernel
+    routed_flop = 6.0 * P * dm * I
     sh_flop = 6.0 * T * dm * cfg.n_shared * cfg.d_ff_shared
     router_flop = 2.0 * T * dm * cfg.n_routed
     gu_ms = st["routed_gate_up"]
-    expert_ms = st["routed_gate_up"] + st["routed_down"]
+    expert_ms = st["routed_gate_up"] + st["routed_down"] + st["shared_gate_up"] + st["shared_down"]
     gu_tflops = gu_flop / (gu_ms * 1e-3) / 1e12
-    expert_tflops = (gu_flop + dn_flop) / (expert_ms * 1e-3) / 1e12
-    layer_tflops = (gu_flop + dn_flop + sh_flop + router_flop) / (ms * 1e-3) / 1e12
+    expert_tflops = (routed_flop + sh_flop) / (expert_ms * 1e-3) / 1e12
+    layer_tflops = (routed_flop + sh_flop + router_flop) / (ms * 1e-3) / 1e12
 
     if args.copy_calibration:
         a = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
@@ -206,7 +213,8 @@ def main():
         "layer_tflops": layer_tflops,
         "stage_ms": st,
         "roofline": {
-            "kernel": "routed gate/up grouped GEMM (grouped_gemm_bf16 gate/up, grouped)",
+            "kernel": "gate/up grouped GEMM (grouped_gemm_bf16 gate/up, grouped; routed experts"
+                      + (" + shared experts as extra groups)" if fold else ")"),
             "bound": "mfma",
             "achieved": gu_tflops,
             "peak": PEAK_BF16_TFLOPS,

@@ -140,7 +140,11 @@ int moe_combine(const moe_layer* layer, int64_t T, const void* y_perm, const int
 
 /* The whole layer: route, dispatch, routed and shared experts, combine.
  * The gather of x rows is fused into the routed gate/up GEMM, so no x_perm
- * is materialised.  residual (NULL or [T, d], usually x itself) is added
+ * is materialised.  When I_s == I the K_s shared experts run inside the
+ * routed gate/up and down launches as K_s extra groups of all T tokens,
+ * and the combine adds their K_s output rows per token (each rounded to
+ * dtype) instead of one y_shared row; otherwise they run as in
+ * moe_shared_ffn.  residual (NULL or [T, d], usually x itself) is added
  * last.  topk_idx, topk_w, counts and offsets are written for inspection
  * and may be NULL (then they live in ws).  y [T, d]. */
 int moe_forward(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
@@ -155,9 +159,11 @@ int moe_forward(const moe_layer* layer, int64_t T, const void* x, const float* w
 enum {
   MOE_STAGE_ROUTE = 0,          /* router logits, softmax, top-K'             */
   MOE_STAGE_DISPATCH = 1,       /* histogram, scan, scatter of row indices    */
-  MOE_STAGE_ROUTED_GATE_UP = 2, /* grouped GEMM x W1/W3 + silu(gate) * up     */
-  MOE_STAGE_ROUTED_DOWN = 3,    /* grouped GEMM H W2                          */
-  MOE_STAGE_SHARED_GATE_UP = 4, /* shared experts, width K_s*I_s (empty if 0) */
+  MOE_STAGE_ROUTED_GATE_UP = 2, /* grouped GEMM x W1/W3 + silu(gate) * up
+                                   (shared experts too when I_s == I)        */
+  MOE_STAGE_ROUTED_DOWN = 3,    /* grouped GEMM H W2 (likewise)               */
+  MOE_STAGE_SHARED_GATE_UP = 4, /* shared experts of width K_s*I_s when
+                                   I_s != I (else empty, as for K_s == 0)    */
   MOE_STAGE_SHARED_DOWN = 5,
   MOE_STAGE_COMBINE = 6
 };

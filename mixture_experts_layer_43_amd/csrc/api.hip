@@ -23,9 +23,20 @@ struct Layout {
 
 size_t elt_bytes(const moe_layer* L) { return L->dtype == MOE_BF16 ? 2 : 4; }
 
+// moe_forward folds the shared experts into the routed grouped launches
+// (K_s extra groups of T rows each) when they have the routed width.
+bool fold_shared(const moe_layer* L) { return L->n_shared > 0 && L->d_ff_shared == L->d_ff; }
+
+// Rows of the H / y_perm matrices in moe_forward: the P routed rows, then
+// K_s blocks of T rows when the shared experts are folded in.
+int64_t forward_rows(const moe_layer* L, int64_t T) {
+  return T * L->top_k + (fold_shared(L) ? T * L->n_shared : 0);
+}
+
 Layout layout_of(const moe_layer* L, int64_t T) {
   Layout o{};
   const size_t P = static_cast<size_t>(T) * L->top_k;
+  const size_t R = static_cast<size_t>(forward_rows(L, T));
   const size_t NB = static_cast<size_t>((T + moe::kCountBlock - 1) / moe::kCountBlock);
   const size_t Nr = L->n_routed, e = elt_bytes(L), d = L->d_model;
   size_t cur = 0;
@@ -43,11 +54,14 @@ Layout layout_of(const moe_layer* L, int64_t T) {
   o.offsets = take((Nr + 1) * 4);
   o.row_token = take(P * 4);
   o.slot_row = take(P * 4);
-  o.h = take(P * L->d_ff * e);
-  o.y_perm = take(P * d * e);
+  // H holds either the forward rows or, for moe_shared_ffn and the unfolded
+  // forward (after the routed GEMMs are done with it), the T x K_s*I_s
+  // shared intermediate.
   const size_t wsh = static_cast<size_t>(L->n_shared) * (L->n_shared > 0 ? L->d_ff_shared : 0);
-  o.h_shared = take(static_cast<size_t>(T) * wsh * e);
-  o.y_shared = take(L->n_shared > 0 ? static_cast<size_t>(T) * d * e : 0);
+  o.h = take(std::max(R * L->d_ff, static_cast<size_t>(T) * wsh) * e);
+  o.h_shared = o.h;
+  o.y_perm = take(R * d * e);
+  o.y_shared = take(L->n_shared > 0 && !fold_shared(L) ? static_cast<size_t>(T) * d * e : 0);
   o.total = cur;
   return o;
 }
@@ -67,10 +81,11 @@ int check_layer(const moe_layer* L, int64_t T) {
   // Every activation and weight matrix must stay below 4 GB (32-bit byte
   // offsets inside the GEMM kernels).
   const int64_t e = static_cast<int64_t>(elt_bytes(L));
-  const int64_t P = T * L->top_k;
+  const int64_t R = forward_rows(L, T);
   const int64_t wsh = static_cast<int64_t>(L->n_shared) * (L->n_shared > 0 ? L->d_ff_shared : 0);
   const int64_t lim = int64_t{1} << 32;
-  if (P * std::max(L->d_model, L->d_ff) * e >= lim || T * wsh * e >= lim ||
+  if (R >= (int64_t{1} << 31)) return MOE_ERR_UNSUPPORTED;
+  if (R * std::max(L->d_model, L->d_ff) * e >= lim || T * wsh * e >= lim ||
       wsh * L->d_model * e >= lim || static_cast<int64_t>(L->d_ff) * L->d_model * e >= lim)
     return MOE_ERR_UNSUPPORTED;
   const int q = (L->dtype == MOE_BF16) ? 64 : 4;
@@ -155,6 +170,22 @@ moe::GemmArgs routed_down(const moe_layer* L, int64_t T, const int32_t* offsets,
   g.ldc = L->d_model;
   g.mode = moe::kDown;
   return g;
+}
+
+// The K_s shared experts as extra groups of T rows after the routed rows
+// (rows P + s*T + t), in the routed gate/up and down launches.
+void add_shared_groups(const moe_layer* L, int64_t T, moe::GemmArgs& g, const void* b0,
+                       const void* b1, bool down) {
+  const int64_t e = elt_bytes(L);
+  g.n_extra = L->n_shared;
+  g.extra_rows = static_cast<int>(T);
+  g.extra_base = T * L->top_k;
+  g.rows_total = forward_rows(L, T);
+  g.Bx0 = b0;
+  g.Bx1 = b1;
+  g.bx_group_stride = static_cast<int64_t>(L->d_ff_shared) * L->d_model;
+  g.bx_bytes = g.bx_group_stride * e;
+  if (down) g.a_bytes = g.rows_total * static_cast<int64_t>(L->d_ff) * e;
 }
 
 int gemm(const moe_layer* L, const moe::GemmArgs& g, hipStream_t s) {
@@ -374,6 +405,7 @@ int moe_combine(const moe_layer* layer, int64_t T, const void* y_perm, const int
   a.slot_row = slot_row;
   a.topk_w = topk_w;
   a.y_shared = y_shared;
+  a.shared_blocks = 1;
   a.residual = residual;
   a.y = y;
   a.T = static_cast<int>(T);
@@ -437,22 +469,49 @@ static int forward_impl(const moe_layer* layer, int64_t T, const void* x,
                        nullptr, ws, lo, s));
   MOE_TRY(m.mark(3));
   // Routed experts; the gather x[row_token[r]] happens inside the A-tile load.
+  moe::GemmArgs gu = routed_gate_up(layer, T, offsets, x, row_token, w_gate, w_up, H);
+  moe::GemmArgs dn = routed_down(layer, T, offsets, H, w_down, y_perm);
+  const bool fold = fold_shared(layer);
+  if (fold) {
+    // Shared experts ride in the routed launches: their rows of y_perm are
+    // summed by the combine, one block of T rows per shared expert.
+    add_shared_groups(layer, T, gu, ws_gate, ws_up, false);
+    add_shared_groups(layer, T, dn, ws_down, nullptr, true);
+  }
   MOE_TRY(m.mark(4));
-  MOE_TRY(gemm(layer, routed_gate_up(layer, T, offsets, x, row_token, w_gate, w_up, H), s));
+  MOE_TRY(gemm(layer, gu, s));
   MOE_TRY(m.mark(5));
   MOE_TRY(m.mark(6));
-  MOE_TRY(gemm(layer, routed_down(layer, T, offsets, H, w_down, y_perm), s));
+  MOE_TRY(gemm(layer, dn, s));
   MOE_TRY(m.mark(7));
   MOE_TRY(m.mark(8));
-  if (layer->n_shared > 0)
+  if (layer->n_shared > 0 && !fold)
     MOE_TRY(gemm(layer, shared_gate_up(layer, T, x, ws_gate, ws_up, h_shared), s));
   MOE_TRY(m.mark(9));
   MOE_TRY(m.mark(10));
-  if (layer->n_shared > 0)
+  if (layer->n_shared > 0 && !fold)
     MOE_TRY(gemm(layer, shared_down(layer, T, h_shared, ws_down, y_shared), s));
   MOE_TRY(m.mark(11));
   MOE_TRY(m.mark(12));
-  MOE_TRY(moe_combine(layer, T, y_perm, slot_row, topk_w, y_shared, residual, y, stream));
+  moe::CombineArgs c{};
+  c.y_perm = y_perm;
+  c.slot_row = slot_row;
+  c.topk_w = topk_w;
+  if (fold) {
+    c.y_shared = static_cast<char*>(y_perm) + T * layer->top_k * layer->d_model * elt_bytes(layer);
+    c.shared_blocks = layer->n_shared;
+    c.shared_stride = T * layer->d_model;
+  } else {
+    c.y_shared = y_shared;
+    c.shared_blocks = 1;
+  }
+  c.residual = residual;
+  c.y = y;
+  c.T = static_cast<int>(T);
+  c.d = layer->d_model;
+  c.top_k = layer->top_k;
+  c.bf16 = layer->dtype == MOE_BF16;
+  MOE_HIP(moe::launch_combine(c, s));
   return m.mark(13);
 }
 

@@ -1,8 +1,9 @@
 // Gate-weighted combine (DeepSeekMoE page, section 3.2, eq. 9):
 //   y_t = sum_j g_{t,j} FFN_{e_j}(u_t) + sum_s FFN^sh_s(u_t) (+ u_t)
-// One wavefront per token; each lane owns 16-byte column chunks, gathers the
-// K' expert rows of the token through slot_row, accumulates in fp32 in
-// ascending j, adds the shared-expert sum and the residual, and rounds once.
+// Each token's K' expert rows are gathered through slot_row and accumulated
+// in fp32 in ascending j, then the shared-expert rows (one sum, or one row
+// per shared expert in order) and the residual are added, and the sum is
+// rounded once.
 // Pure streaming: bound by HBM bandwidth.
 #include "common.h"
 #include "kernels.h"
@@ -10,8 +11,6 @@
 namespace moe {
 
 namespace {
-
-constexpr int kMaxK = 16;
 
 template <typename T>
 struct Vec16;  // 16 bytes of T as fp32 lanes
@@ -48,54 +47,91 @@ struct Vec16<float> {
   }
 };
 
-template <typename E>
+// One wavefront per token; lane l owns the 16-byte column chunks
+// l, l + 64, ... (CPL of them per pass over 64*CPL chunks).  The rows to sum are the K' routed rows
+// (weight topk_w), then the shared-expert rows and the residual (weight 1),
+// taken JG at a time with all their loads in flight before any is used.
+template <typename E, int CPL>
 __global__ __launch_bounds__(256) void combine_kernel(
     const char* __restrict__ y_perm, const int32_t* __restrict__ slot_row,
     const float* __restrict__ topk_w, const char* __restrict__ y_shared,
-    const char* __restrict__ residual, char* __restrict__ y, int T, int chunks, int K) {
+    int shared_blocks, int64_t shared_stride_bytes, const char* __restrict__ residual,
+    char* __restrict__ y, int T, int chunks, int K) {
   using V = Vec16<E>;
   constexpr int N = V::N;
+  constexpr int JG = CPL <= 4 ? 4 : 2;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t t = static_cast<int64_t>(blockIdx.x) * (256 / kWave) + threadIdx.x / kWave;
   if (t >= T) return;
   const int64_t row_bytes = static_cast<int64_t>(chunks) * 16;
-  int64_t src[kMaxK];
-  float w[kMaxK];
+  const int nrows = K + shared_blocks + (residual != nullptr ? 1 : 0);
+  for (int cb = 0; cb < chunks; cb += kWave * CPL) {
+  float acc[CPL][N];
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    if (j < K) {
-      src[j] = static_cast<int64_t>(slot_row[t * K + j]) * row_bytes;
-      w[j] = topk_w[t * K + j];
-    }
-  }
-  for (int c = lane; c < chunks; c += kWave) {
-    const int64_t cb = static_cast<int64_t>(c) * 16;
-    float acc[N];
+  for (int i = 0; i < CPL; ++i)
 #pragma unroll
-    for (int i = 0; i < N; ++i) acc[i] = 0.0f;
+    for (int n = 0; n < N; ++n) acc[i][n] = 0.0f;
+  for (int j0 = 0; j0 < nrows; j0 += JG) {
+    // Branch-free issue (so all loads of the group are in flight together):
+    // rows past the end re-read the last row, columns past the end re-read
+    // the last chunk; neither is used.
+    float v[JG][CPL][N];
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      if (j < K) {
-        float v[N];
-        V::load(y_perm + src[j] + cb, v);
+    for (int jj = 0; jj < JG; ++jj) {
+      const int j = min(j0 + jj, nrows - 1);
+      const char* routed = y_perm + static_cast<int64_t>(slot_row[t * K + min(j, K - 1)]) * row_bytes;
+      const char* shared = (shared_blocks > 0 ? y_shared : y_perm) +
+                           max(j - K, 0) * shared_stride_bytes + t * row_bytes;
+      const char* res = (residual != nullptr ? residual : y_perm) + t * row_bytes;
+      const char* row = j < K ? routed : (j < K + shared_blocks ? shared : res);
 #pragma unroll
-        for (int i = 0; i < N; ++i) acc[i] = fmaf(w[j], v[i], acc[i]);
+      for (int i = 0; i < CPL; ++i) {
+        const int c = min(cb + lane + kWave * i, chunks - 1);
+        V::load(row + static_cast<int64_t>(c) * 16, v[jj][i]);
       }
     }
-    if (y_shared) {
-      float v[N];
-      V::load(y_shared + t * row_bytes + cb, v);
 #pragma unroll
-      for (int i = 0; i < N; ++i) acc[i] += v[i];
-    }
-    if (residual) {
-      float v[N];
-      V::load(residual + t * row_bytes + cb, v);
+    for (int jj = 0; jj < JG; ++jj) {
+      const int j = j0 + jj;
+      if (j >= nrows) break;
+      const float w = j < K ? topk_w[t * K + j] : 1.0f;
 #pragma unroll
-      for (int i = 0; i < N; ++i) acc[i] += v[i];
+      for (int i = 0; i < CPL; ++i)
+#pragma unroll
+        for (int n = 0; n < N; ++n) acc[i][n] = fmaf(w, v[jj][i][n], acc[i][n]);
     }
-    V::store(y + t * row_bytes + cb, acc);
   }
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = cb + lane + kWave * i;
+    if (c < chunks) V::store(y + t * row_bytes + static_cast<int64_t>(c) * 16, acc[i]);
+  }
+  }
+}
+
+template <typename E>
+hipError_t launch_combine_t(const CombineArgs& a, int chunks, hipStream_t s) {
+  const int grid = (a.T + 3) / 4;
+  const int blocks = a.y_shared ? a.shared_blocks : 0;
+  const int64_t stride = a.shared_stride * static_cast<int64_t>(sizeof(E));
+  const char* yp = static_cast<const char*>(a.y_perm);
+  const char* ys = static_cast<const char*>(a.y_shared);
+  const char* res = static_cast<const char*>(a.residual);
+  char* y = static_cast<char*>(a.y);
+  const int cpl = (chunks + kWave - 1) / kWave;
+  if (cpl <= 1)
+    hipLaunchKernelGGL((combine_kernel<E, 1>), dim3(grid), dim3(256), 0, s, yp, a.slot_row, a.topk_w,
+                       ys, blocks, stride, res, y, a.T, chunks, a.top_k);
+  else if (cpl <= 2)
+    hipLaunchKernelGGL((combine_kernel<E, 2>), dim3(grid), dim3(256), 0, s, yp, a.slot_row, a.topk_w,
+                       ys, blocks, stride, res, y, a.T, chunks, a.top_k);
+  else if (cpl <= 4)
+    hipLaunchKernelGGL((combine_kernel<E, 4>), dim3(grid), dim3(256), 0, s, yp, a.slot_row, a.topk_w,
+                       ys, blocks, stride, res, y, a.T, chunks, a.top_k);
+  else  // rows longer than 8 KB take several passes of 512 chunks
+    hipLaunchKernelGGL((combine_kernel<E, 8>), dim3(grid), dim3(256), 0, s, yp, a.slot_row, a.topk_w,
+                       ys, blocks, stride, res, y, a.T, chunks, a.top_k);
+  return hipGetLastError();
 }
 
 __global__ __launch_bounds__(256) void zero_kernel(uint32_t* p, int64_t words) {
@@ -110,18 +146,7 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   const int elt = a.bf16 ? 2 : 4;
   const int chunks = static_cast<int>(static_cast<int64_t>(a.d) * elt / 16);
-  const int grid = (a.T + 3) / 4;
-  if (a.bf16)
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(grid), dim3(256), 0, s,
-                       static_cast<const char*>(a.y_perm), a.slot_row, a.topk_w,
-                       static_cast<const char*>(a.y_shared), static_cast<const char*>(a.residual),
-                       static_cast<char*>(a.y), a.T, chunks, a.top_k);
-  else
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(grid), dim3(256), 0, s,
-                       static_cast<const char*>(a.y_perm), a.slot_row, a.topk_w,
-                       static_cast<const char*>(a.y_shared), static_cast<const char*>(a.residual),
-                       static_cast<char*>(a.y), a.T, chunks, a.top_k);
-  return hipGetLastError();
+  return a.bf16 ? launch_combine_t<bf16_t>(a, chunks, s) : launch_combine_t<float>(a, chunks, s);
 }
 
 // Fill kernel instead of hipMemsetAsync so a caller may capture it in a graph.

@@ -260,11 +260,15 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
     // Row tiles per group are known only on the device.  Each wavefront
     // scans the groups 64 at a time (per-lane tile counts, shuffle prefix
     // sums, ballot) - first for the total, then for the group of its tile.
-    const int G = p.n_groups;
+    // The extra groups follow the indexed ones.
+    const int G = p.n_groups + p.n_extra;
+    auto group_rows = [&](int gi) {
+      return gi < p.n_groups ? p.offsets[gi + 1] - p.offsets[gi] : (gi < G ? p.extra_rows : 0);
+    };
     int total = 0;
     for (int g0 = 0; g0 < G; g0 += kWave) {
       const int gi = g0 + lane;
-      const int m = gi < G ? p.offsets[gi + 1] - p.offsets[gi] : 0;
+      const int m = group_rows(gi);
       int c = (m + BM - 1) / BM;
 #pragma unroll
       for (int o = kWave / 2; o > 0; o >>= 1) c += __shfl_xor(c, o, kWave);
@@ -286,7 +290,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
     int base = 0;
     for (int g0 = 0; g0 < G; g0 += kWave) {
       const int gi = g0 + lane;
-      const int m = gi < G ? p.offsets[gi + 1] - p.offsets[gi] : 0;
+      const int m = group_rows(gi);
       const int cnt = (m + BM - 1) / BM;
       int incl = cnt;
 #pragma unroll
@@ -300,8 +304,11 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
         const int src = __ffsll(static_cast<unsigned long long>(hit)) - 1;
         g = g0 + src;
         const int first = base + __shfl(excl, src, kWave);
-        row0 = p.offsets[g] + (mt - first) * BM;
-        rows = min(BM, p.offsets[g + 1] - row0);
+        const int64_t gstart = g < p.n_groups
+                                   ? p.offsets[g]
+                                   : p.extra_base + static_cast<int64_t>(g - p.n_groups) * p.extra_rows;
+        row0 = static_cast<int>(gstart) + (mt - first) * BM;
+        rows = min(BM, group_rows(g) - (mt - first) * BM);
         break;
       }
       base += __shfl(incl, kWave - 1, kWave);
@@ -313,10 +320,14 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
   }
 
   const bf16_t* A = static_cast<const bf16_t*>(p.A);
-  const bf16_t* B0 = static_cast<const bf16_t*>(p.B0) + static_cast<int64_t>(g) * p.b_group_stride;
-  const bf16_t* B1 = (MODE == kGateUp)
-                         ? static_cast<const bf16_t*>(p.B1) + static_cast<int64_t>(g) * p.b_group_stride
-                         : nullptr;
+  const bool extra = GROUPED && g >= p.n_groups;
+  const int64_t gx = extra ? g - p.n_groups : g;
+  const bf16_t* B0 = static_cast<const bf16_t*>(extra ? p.Bx0 : p.B0) +
+                     gx * (extra ? p.bx_group_stride : p.b_group_stride);
+  const bf16_t* B1 = (MODE == kGateUp) ? static_cast<const bf16_t*>(extra ? p.Bx1 : p.B1) +
+                                             gx * (extra ? p.bx_group_stride : p.b_group_stride)
+                                       : nullptr;
+  const int64_t b_bytes = extra ? p.bx_bytes : p.b_bytes;
 
   // ---- per-lane source chunks (fixed over K) -----------------------------
   // One load moves 64 lanes x 16 B into a contiguous 1 KB of LDS: RPL tile
@@ -335,13 +346,13 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
     const int r = (wv * A_LD + i) * RPL + lr;
     const int c = lp ^ swz<BK>(r);
     const int64_t grow = row0 + min(r, rows - 1);
-    const int64_t arow = p.gather ? p.gather[grow] : grow;
+    const int64_t arow = !p.gather ? grow : extra ? (grow - p.extra_base) % p.extra_rows : p.gather[grow];
     a_off[i] = static_cast<uint32_t>((arow * p.lda + c * 8) * 2);
   }
   // All B rows one wavefront copies come from the same matrix (W1 or W3 in
   // gate/up mode: the wavefront's RPL*B_LD rows never straddle the boundary).
   const bool up = (MODE == kGateUp) && (wv * B_LD * RPL >= BN / 2);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(up ? B1 : B0, static_cast<uint32_t>(p.b_bytes));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(up ? B1 : B0, static_cast<uint32_t>(b_bytes));
   uint32_t b_off[B_LD];
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) {
@@ -453,7 +464,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
     max_mtiles = (a.rows_total + BM - 1) / BM;
   } else {
     // sum_g ceil(M_g / BM) <= (sum_g M_g + G*(BM-1)) / BM
-    max_mtiles = (a.rows_total + static_cast<int64_t>(a.n_groups) * (BM - 1)) / BM;
+    max_mtiles = (a.rows_total + static_cast<int64_t>(a.n_groups + a.n_extra) * (BM - 1)) / BM;
   }
   const int64_t grid = max_mtiles * n_ntiles;
   if (grid == 0) return hipSuccess;
@@ -474,7 +485,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.rows_total == 0) return hipSuccess;
-  const int64_t mean_rows = a.rows_total / (a.offsets ? a.n_groups : 1);
+  const int64_t mean_rows = a.rows_total / (a.offsets ? a.n_groups + a.n_extra : 1);
   if (mean_rows >= 192) return launch_cfg<256, 256, 2, 4, 64, 2>(a, s);
   if (mean_rows >= 64) return launch_cfg<128, 256, 2, 2, 64, 2>(a, s);
   return launch_cfg<32, 256, 1, 4, 64, 2>(a, s);

@@ -29,12 +29,23 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(GemmArgs p) {
        i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     const int64_t r = i / p.N;
     const int n = static_cast<int>(i % p.N);
-    const int g = p.offsets ? find_group(p.offsets, p.n_groups, r) : 0;
-    const int64_t arow = p.gather ? p.gather[r] : r;
+    const bool extra = p.n_extra > 0 && r >= p.extra_base;
+    const float* b0;
+    const float* b1 = nullptr;
+    int64_t arow;
+    if (extra) {
+      const int64_t s = (r - p.extra_base) / p.extra_rows;
+      b0 = static_cast<const float*>(p.Bx0) + s * p.bx_group_stride + n * p.ldb;
+      if (MODE == kGateUp) b1 = static_cast<const float*>(p.Bx1) + s * p.bx_group_stride + n * p.ldb;
+      arow = p.gather ? (r - p.extra_base) % p.extra_rows : r;
+    } else {
+      const int g = p.offsets ? find_group(p.offsets, p.n_groups, r) : 0;
+      b0 = static_cast<const float*>(p.B0) + g * p.b_group_stride + n * p.ldb;
+      if (MODE == kGateUp) b1 = static_cast<const float*>(p.B1) + g * p.b_group_stride + n * p.ldb;
+      arow = p.gather ? p.gather[r] : r;
+    }
     const float* a = A + arow * p.lda;
-    const float* b0 = static_cast<const float*>(p.B0) + g * p.b_group_stride + n * p.ldb;
     if (MODE == kGateUp) {
-      const float* b1 = static_cast<const float*>(p.B1) + g * p.b_group_stride + n * p.ldb;
       float s0 = 0.0f, s1 = 0.0f;
       for (int k = 0; k < p.K; ++k) {
         const int64_t bo = static_cast<int64_t>(k / p.k_sub) * p.b_sub_stride + (k % p.k_sub);

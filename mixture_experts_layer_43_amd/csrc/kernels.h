@@ -44,6 +44,12 @@ enum GemmMode { kGateUp = 0, kDown = 1 };
 // B + g*b_group_stride + (k / k_sub)*b_sub_stride + n*ldb + (k % k_sub).
 // kGateUp: C[r, n] = silu(A_r . B0_n) * (A_r . B1_n), n < N.
 // kDown:   C[r, n] = A_r . B0_n.
+//
+// Extra groups (grouped calls only; the shared experts folded into the
+// routed launch): group n_groups + s, s < n_extra, holds rows
+// [extra_base + s*extra_rows, extra_base + (s+1)*extra_rows), takes B from
+// Bx0/Bx1 + s*bx_group_stride (bx_bytes per matrix), and with a gather its
+// row r reads A row (r - extra_base) % extra_rows (every token once).
 struct GemmArgs {
   int64_t a_bytes;         // bytes of A readable through row indices (< 4 GB)
   int64_t b_bytes;         // bytes of one group's B0 (and of its B1) (< 4 GB)
@@ -61,6 +67,12 @@ struct GemmArgs {
   void* C;
   int64_t ldc;
   int mode;
+  int n_extra;
+  int extra_rows;
+  int64_t extra_base;
+  const void* Bx0;
+  const void* Bx1;
+  int64_t bx_group_stride, bx_bytes;
 };
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
@@ -70,7 +82,9 @@ struct CombineArgs {
   const void* y_perm;       // [P, d]
   const int32_t* slot_row;  // [P]
   const float* topk_w;      // [T, K']
-  const void* y_shared;     // [T, d] or null
+  const void* y_shared;     // shared_blocks x [T, d] (shared_stride elements apart) or null
+  int shared_blocks;
+  int64_t shared_stride;
   const void* residual;     // [T, d] or null
   void* y;                  // [T, d]
   int T, d, top_k;

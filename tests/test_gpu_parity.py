@@ -35,6 +35,9 @@ MID = {
                               top_k=16, d_ff=64, d_ff_shared=64, seed=106),
     "mid-many-experts": LayerConfig(name="mid-many-experts", tokens=300, d_model=128, n_routed=200,
                                     n_shared=0, top_k=8, d_ff=64, d_ff_shared=64, seed=107),
+    # More tokens than the single-workgroup dispatch takes (1024).
+    "mid-many-tokens": LayerConfig(name="mid-many-tokens", tokens=2500, d_model=64, n_routed=24,
+                                   n_shared=1, top_k=5, d_ff=64, d_ff_shared=64, seed=108),
 }
 FULL_ORACLE = ["tiny-f32", "16b-decode", *MID]
 SAMPLED = ["2b", "16b", "gshard-zipf"]
@@ -89,7 +92,8 @@ def test_route_alone(name):
     check_gates(host(w), ref["topk_w"])
 
 
-@pytest.mark.parametrize("name", ["tiny-f32", "mid-ragged", "mid-smallm", "mid-wide-k", "16b-decode"])
+@pytest.mark.parametrize("name", ["tiny-f32", "mid-ragged", "mid-smallm", "mid-wide-k", "16b-decode",
+                                  "mid-many-tokens"])
 def test_permute_alone_is_bit_exact(name):
     cfg, inp, ref = case(name)
     announce(f"permute {name}")
@@ -102,7 +106,8 @@ def test_permute_alone_is_bit_exact(name):
     xs = d["x"].view(torch.int16 if cfg.dtype == "bf16" else torch.int32).cpu().numpy()
     np.testing.assert_array_equal(xp, xs[ref["row_token"]])
     nox = ops.permute(ops.Layer.of(cfg), idx, None)
-    np.testing.assert_array_equal(host(nox["slot_row"]), ref["slot_row"])
+    for k in ("counts", "offsets", "row_token", "slot_row"):
+        np.testing.assert_array_equal(host(nox[k]), ref[k], err_msg=f"{k} (no row copy)")
 
 
 def ref_rows(cfg, inp, ref):
