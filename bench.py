@@ -6,14 +6,17 @@
 A step is one moe_forward (router, dispatch, routed gate/up and down grouped
 GEMMs, shared experts, combine) over one batch of seeded synthetic inputs
 that are resident in HBM before timing starts.  The timed steps run through
-moe_forward_timed, which records a HIP event pair around every stage on the
-launch stream, so per-stage GPU times come from the timed region itself.
+moe_forward_timed with a HIP event pair around the gate/up kernel only (on
+the launch stream); the per-stage breakdown comes from a few further steps
+with every marker set, outside the timed region.
 
 Prints one JSON line.  `roofline` is for the dominant kernel, the gate/up
-grouped GEMM: algorithmic FLOPs 4*R*d*I per launch over its event-timed
-duration, against the bf16 dense MFMA peak.  R = T*K' routed rows, plus
-K_s*T rows when the shared experts (of the routed width) ride in the same
-launch.  `expert_gemm_tflops` counts all expert FLOPs (routed 6*T*K'*d*I
+grouped GEMM, whose launch does 4*R*d*I FLOPs (R = T*K' routed rows, plus
+K_s*T rows when the shared experts of the routed width ride in the same
+launch) and must move, at the least, the W1/W3 rows of every expert it
+uses, the x rows it reads and the R*I outputs it writes.  Above the ridge
+point (peak FLOP/s over peak bytes/s) it is priced against the bf16 dense
+MFMA peak, below it against HBM bandwidth.  `expert_gemm_tflops` counts all expert FLOPs (routed 6*T*K'*d*I
 and shared 6*T*d*K_s*I_s) over the four GEMM stages.  `cpu_baseline` times
 the fp64 oracle on the first --cpu-tokens tokens of the same workload on
 the host cores.
@@ -126,42 +129,61 @@ def main():
 
     hip = hip_runtime()
     nev = 2 * _lib.MOE_NUM_STAGES
-    events = []
-    for _ in range(args.steps):
+    gu_stage = _lib.STAGES.index("routed_gate_up")
+    created = []
+
+    def markers(stages):
+        """Event array for moe_forward_timed with handles for `stages` only."""
         arr = (ctypes.c_void_p * nev)()
-        for i in range(nev):
-            ev = ctypes.c_void_p()
-            assert hip.hipEventCreate(ctypes.byref(ev)) == 0
-            arr[i] = ev.value
-        events.append(arr)
+        for st_i in stages:
+            for i in (2 * st_i, 2 * st_i + 1):
+                ev = ctypes.c_void_p()
+                assert hip.hipEventCreate(ctypes.byref(ev)) == 0
+                arr[i] = ev.value
+                created.append(ev.value)
+        return arr
+
+    def elapsed(arr, st_i):
+        f = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(f), arr[2 * st_i], arr[2 * st_i + 1]) == 0
+        return f.value
 
     p = ops._p
     lib = _lib.lib()
     c_layer = lay.c()
     stream = ops._stream()
+
+    def step(arr):
+        _lib.check("moe_forward_timed", lib.moe_forward_timed(
+            ctypes.byref(c_layer), cfg.tokens, p(d["x"]), p(d["w_router"]), p(d["bias"]),
+            p(d["w_gate"]), p(d["w_up"]), p(d["w_down"]), p(d["ws_gate"]), p(d["ws_up"]),
+            p(d["ws_down"]), None, p(fwd.y), p(fwd.topk_idx), p(fwd.topk_w), p(fwd.counts),
+            p(fwd.offsets), p(fwd.ws), fwd.ws.numel(), stream, arr))
+
+    # Timed region: whole-layer steps; HIP events mark only the gate/up kernel.
+    timed = [markers([gu_stage]) for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for k in range(args.steps):
-        _lib.check("moe_forward_timed", lib.moe_forward_timed(
-            ctypes.byref(c_layer), cfg.tokens, p(d["x"]), p(d["w_router"]), p(d["bias"]),
-            p(d["w_gate"]), p(d["w_up"]), p(d["w_down"]), p(d["ws_gate"]), p(d["ws_up"]),
-            p(d["ws_down"]), None, p(fwd.y), p(fwd.topk_idx), p(fwd.topk_w), p(fwd.counts),
-            p(fwd.offsets), p(fwd.ws), fwd.ws.numel(), stream, events[k]))
+        step(timed[k])
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms = total_ms / args.steps
+    gu_ms = float(np.mean([elapsed(arr, gu_stage) for arr in timed]))
 
-    stage_ms = np.zeros((args.steps, _lib.MOE_NUM_STAGES))
-    f = ctypes.c_float()
-    for k, arr in enumerate(events):
-        for s in range(_lib.MOE_NUM_STAGES):
-            assert hip.hipEventElapsedTime(ctypes.byref(f), arr[2 * s], arr[2 * s + 1]) == 0
-            stage_ms[k, s] = f.value
-        for i in range(nev):
-            hip.hipEventDestroy(arr[i])
+    # Per-stage breakdown from separate steps after the timed region (every
+    # marker costs a few microseconds of GPU time, so they stay out of it).
+    n_brk = max(3, min(args.steps, 10))
+    brk = [markers(range(_lib.MOE_NUM_STAGES)) for _ in range(n_brk)]
+    for arr in brk:
+        step(arr)
+    torch.cuda.synchronize()
+    stage_ms = np.array([[elapsed(arr, st_i) for st_i in range(_lib.MOE_NUM_STAGES)] for arr in brk])
+    for ev in created:
+        hip.hipEventDestroy(ev)
     st = dict(zip(_lib.STAGES, stage_ms.mean(0).round(5).tolist()))
 
     T, dm, I, K = cfg.tokens, cfg.d_model, cfg.d_ff, cfg.top_k
@@ -174,11 +196,27 @@ def main():
     routed_flop = 6.0 * P * dm * I
     sh_flop = 6.0 * T * dm * cfg.n_shared * cfg.d_ff_shared
     router_flop = 2.0 * T * dm * cfg.n_routed
-    gu_ms = st["routed_gate_up"]
-    expert_ms = st["routed_gate_up"] + st["routed_down"] + st["shared_gate_up"] + st["shared_down"]
+    expert_ms = st["routed_gate_up"] + st["routed_down"]
+    if not fold:
+        expert_ms += st["shared_gate_up"] + st["shared_down"]
     gu_tflops = gu_flop / (gu_ms * 1e-3) / 1e12
+    # Least bytes the gate/up launch moves: W1 and W3 rows of the experts it
+    # uses (all of them at these batch sizes), x once, and the R x I outputs.
+    n_w = cfg.n_routed + (cfg.n_shared if fold else 0)
+    gu_bytes = 2.0 * (2 * n_w * I * dm + T * dm + rows * I)
+    gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
+    mfma_bound = gu_flop / gu_bytes >= (PEAK_BF16_TFLOPS * 1e12) / (PEAK_HBM_GBS * 1e9)
     expert_tflops = (routed_flop + sh_flop) / (expert_ms * 1e-3) / 1e12
     layer_tflops = (routed_flop + sh_flop + router_flop) / (ms * 1e-3) / 1e12
+
+    # Whole-layer HBM view (the decode-shaped layer is bound by it): the
+    # least bytes a forward moves are the weights of every expert it uses,
+    # the router weights, x and y.
+    touched = int((fwd.counts.cpu().numpy() > 0).sum())
+    esz = 2 if cfg.dtype == "bf16" else 4
+    layer_bytes = (3.0 * esz * dm * (touched * I + cfg.n_shared * cfg.d_ff_shared)
+                   + 4.0 * cfg.n_routed * dm + 2.0 * esz * T * dm)
+    layer_gbs = layer_bytes / (ms * 1e-3) / 1e9
 
     if args.copy_calibration:
         a = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
@@ -212,16 +250,20 @@ def main():
         "expert_gemm_frac_mfma": expert_tflops / PEAK_BF16_TFLOPS,
         "layer_tflops": layer_tflops,
         "stage_ms": st,
+        "layer_algorithmic_bytes": layer_bytes,
+        "layer_hbm_gbs": layer_gbs,
+        "layer_hbm_frac": layer_gbs / PEAK_HBM_GBS,
         "roofline": {
             "kernel": "gate/up grouped GEMM (grouped_gemm_bf16 gate/up, grouped; routed experts"
                       + (" + shared experts as extra groups)" if fold else ")"),
-            "bound": "mfma",
-            "achieved": gu_tflops,
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": gu_tflops / PEAK_BF16_TFLOPS,
+            "bound": "mfma" if mfma_bound else "hbm",
+            "achieved": gu_tflops if mfma_bound else gu_gbs,
+            "peak": PEAK_BF16_TFLOPS if mfma_bound else PEAK_HBM_GBS,
+            "unit": "TFLOP/s" if mfma_bound else "GB/s",
+            "frac": gu_tflops / PEAK_BF16_TFLOPS if mfma_bound else gu_gbs / PEAK_HBM_GBS,
             "traffic": TRAFFIC_BYTES.get(cfg.name),
             "algorithmic_flop_per_launch": gu_flop,
+            "algorithmic_bytes_per_launch": gu_bytes,
             "avg_launch_ms": gu_ms,
         },
     }

@@ -172,8 +172,9 @@ enum {
  * holds 2*MOE_NUM_STAGES hipEvent_t handles (as void*) created by the caller;
  * events[2s] and events[2s+1] are recorded on `stream` right before and
  * right after stage s, so hipEventElapsedTime(events[2s], events[2s+1]) is
- * that stage's GPU time.  A NULL array or handle is MOE_ERR_INVALID_ARG.
- * Everything else is exactly moe_forward. */
+ * that stage's GPU time.  A NULL handle skips that marker (to time only
+ * some stages); a NULL array is MOE_ERR_INVALID_ARG.  Everything else is
+ * exactly moe_forward. */
 int moe_forward_timed(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
                       const float* logit_bias, const void* w_gate, const void* w_up,
                       const void* w_down, const void* ws_gate, const void* ws_up,
