@@ -25,6 +25,7 @@ namespace moe {
 namespace {
 
 constexpr int kXcds = 8;
+constexpr int kPanel = 8;   // row tiles per panel in the grouped tile order
 
 // Buffer resource over `bytes` bytes at `base` (raw buffer: offsets are byte
 // offsets; loads past `bytes` return zero instead of faulting).
@@ -244,9 +245,10 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
   const int n_ntiles = (p.N + OUT_N - 1) / OUT_N;
 
   // ---- locate (group, first row, rows) of this workgroup's tile ---------
-  // Tiles are ordered row tile major (the n_ntiles column tiles of one row
-  // tile are consecutive), and consecutive tiles go to the same XCD so they
-  // share its L2: the remap spreads the real tiles evenly over the XCDs.
+  // Consecutive tiles go to the same XCD so they share its L2: the remap
+  // spreads the real tiles evenly over the XCDs, in contiguous ranges.  A
+  // dense call orders tiles row tile major; grouped calls order them by
+  // panels (below).
   int g, row0, rows, mt, nt;
   if (!GROUPED) {
     const int bid = xcd_remap(blockIdx.x, gridDim.x);
@@ -282,16 +284,19 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
     const int base_n = real / kXcds, rem = real % kXcds;
     if (local >= base_n + (xcd < rem ? 1 : 0)) return;
     const int bid = xcd * base_n + min(xcd, rem) + local;
-    mt = bid / n_ntiles;
-    nt = bid % n_ntiles;
+    // Order inside a group: panels of up to kPanel row tiles; inside a
+    // panel the column tile is the slow index, so the workgroups running
+    // together on an XCD share a few column tiles of the weights (read from
+    // HBM once per panel) and the panel's rows of A.
     g = -1;
     row0 = 0;
     rows = 0;
+    mt = 0;
+    nt = 0;
     int base = 0;
     for (int g0 = 0; g0 < G; g0 += kWave) {
       const int gi = g0 + lane;
-      const int m = group_rows(gi);
-      const int cnt = (m + BM - 1) / BM;
+      const int cnt = (group_rows(gi) + BM - 1) / BM * n_ntiles;  // tiles of group gi
       int incl = cnt;
 #pragma unroll
       for (int o = 1; o < kWave; o <<= 1) {
@@ -299,20 +304,28 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
         if (lane >= o) incl += v;
       }
       const int excl = incl - cnt;
-      const uint64_t hit = __ballot(mt >= base + excl && mt < base + incl);
+      const uint64_t hit = __ballot(bid >= base + excl && bid < base + incl);
       if (hit != 0) {
         const int src = __ffsll(static_cast<unsigned long long>(hit)) - 1;
         g = g0 + src;
-        const int first = base + __shfl(excl, src, kWave);
+        const int in_g = bid - base - __shfl(excl, src, kWave);
+        const int gm = group_rows(g);
+        const int mtg = (gm + BM - 1) / BM;
+        const int panel = in_g / (kPanel * n_ntiles);
+        const int pm = min(kPanel, mtg - panel * kPanel);
+        const int r = in_g - panel * kPanel * n_ntiles;
+        nt = r / pm;
+        const int mloc = panel * kPanel + r % pm;
         const int64_t gstart = g < p.n_groups
                                    ? p.offsets[g]
                                    : p.extra_base + static_cast<int64_t>(g - p.n_groups) * p.extra_rows;
-        row0 = static_cast<int>(gstart) + (mt - first) * BM;
-        rows = min(BM, group_rows(g) - (mt - first) * BM);
+        row0 = static_cast<int>(gstart) + mloc * BM;
+        rows = min(BM, gm - mloc * BM);
         break;
       }
       base += __shfl(incl, kWave - 1, kWave);
     }
+    nt = __builtin_amdgcn_readfirstlane(nt);
     g = __builtin_amdgcn_readfirstlane(g);
     if (g < 0) return;
     row0 = __builtin_amdgcn_readfirstlane(row0);
