@@ -17,7 +17,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t block_counts, block_base, local_rank, topk_idx, topk_w, counts, offsets, row_token,
+  size_t router_part, block_counts, block_base, local_rank, topk_idx, topk_w, counts, offsets, row_token,
       slot_row, h, y_perm, h_shared, y_shared, total;
 };
 
@@ -45,6 +45,7 @@ Layout layout_of(const moe_layer* L, int64_t T) {
     cur += align_up(bytes);
     return at;
   };
+  o.router_part = take(moe::router_partial_bytes(T));
   o.block_counts = take(NB * Nr * 4);
   o.block_base = take(NB * Nr * 4);
   o.local_rank = take(P * 4);
@@ -277,8 +278,9 @@ int moe_workspace_size(const moe_layer* layer, int64_t T, size_t* bytes) {
   return MOE_OK;
 }
 
-int moe_route(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
-              const float* logit_bias, int32_t* topk_idx, float* topk_w, void* stream) {
+static int route_impl(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
+                      const float* logit_bias, int32_t* topk_idx, float* topk_w, float* partial,
+                      void* stream) {
   MOE_TRY(check_layer(layer, T));
   MOE_TRY(needT(x, T));
   MOE_TRY(need(w_router));
@@ -287,6 +289,7 @@ int moe_route(const moe_layer* layer, int64_t T, const void* x, const float* w_r
   MOE_TRY(needT(topk_w, T));
   if (T == 0) return MOE_OK;
   moe::RouteArgs a{};
+  a.partial = partial;
   a.x = x;
   a.w_router = w_router;
   a.bias = logit_bias;
@@ -300,6 +303,11 @@ int moe_route(const moe_layer* layer, int64_t T, const void* x, const float* w_r
   a.topk_w = topk_w;
   MOE_HIP(moe::launch_route(a, static_cast<hipStream_t>(stream)));
   return MOE_OK;
+}
+
+int moe_route(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
+              const float* logit_bias, int32_t* topk_idx, float* topk_w, void* stream) {
+  return route_impl(layer, T, x, w_router, logit_bias, topk_idx, topk_w, nullptr, stream);
 }
 
 static int permute_impl(const moe_layer* layer, int64_t T, const int32_t* topk_idx,
@@ -462,7 +470,9 @@ static int forward_impl(const moe_layer* layer, int64_t T, const void* x,
   void* y_shared = layer->n_shared > 0 ? at(ws, lo.y_shared) : nullptr;
 
   MOE_TRY(m.mark(0));
-  MOE_TRY(moe_route(layer, T, x, w_router, logit_bias, topk_idx, topk_w, stream));
+  // With the workspace at hand, small batches may split the router's K.
+  MOE_TRY(route_impl(layer, T, x, w_router, logit_bias, topk_idx, topk_w,
+                     reinterpret_cast<float*>(at(ws, lo.router_part)), stream));
   MOE_TRY(m.mark(1));
   MOE_TRY(m.mark(2));
   MOE_TRY(permute_impl(layer, T, topk_idx, nullptr, counts, offsets, row_token, slot_row,

@@ -15,7 +15,14 @@ struct RouteArgs {
   bool x_bf16;
   int32_t* topk_idx;       // [T, K']
   float* topk_w;           // [T, K']
+  float* partial;          // null, or scratch of router_partial_bytes(T) for split-K logits
 };
+// Split-K of the matrix-core router for small batches: at most this many
+// K slices, each writing a [T, 128] fp32 partial tile.
+constexpr int kRouterSplit = 8;
+inline size_t router_partial_bytes(int64_t T) {
+  return T < 4096 ? static_cast<size_t>(kRouterSplit) * static_cast<size_t>(T) * 128 * 4 : 0;
+}
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 
 // ---- dispatch (dispatch.hip) ----

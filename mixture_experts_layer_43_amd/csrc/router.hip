@@ -249,19 +249,51 @@ __device__ __forceinline__ void router_mma(f32x16 (&acc)[MBLK][NBLK], const bf16
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], bp[nb][q], acc[mb][nb], 0, 0, 0);
 }
 
+// R consecutive K slices starting at slice rs: every x fragment is loaded
+// up front (one trip to HBM), W_g streams through a ring of min(RD, R)
+// slices.  No branches, so every wait on a load is an exact count.
+template <int R, int RD, int MBLK, int NBLK>
+__device__ __forceinline__ void router_round(f32x16 (&acc)[MBLK][NBLK],
+                                             const bf16_t* const (&xp)[MBLK],
+                                             const float* const (&wp)[NBLK], const bool (&ev)[NBLK],
+                                             int rs) {
+  constexpr int D = RD < R ? RD : R;
+  bf16x8 xa[R][MBLK];
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int mb = 0; mb < MBLK; ++mb) xa[i][mb] = *reinterpret_cast<const bf16x8*>(xp[mb] + (rs + i) * 16);
+  float4 wr[D][NBLK][2];
+#pragma unroll
+  for (int i = 0; i < D; ++i) load_w_slice<NBLK>(wr[i], wp, (rs + i) * 16);
+  // Keep every load above at the top: the scheduler would otherwise sink
+  // them next to their first use and serialise the round trips.
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    router_mma<MBLK, NBLK>(acc, xa[i], wr[i % D], ev);
+    if (i + D < R) load_w_slice<NBLK>(wr[i % D], wp, (rs + i + D) * 16);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // One workgroup: 32*MBLK tokens x 32*NBLK experts, kRW wavefronts.  The
 // d/16 K slices are cut into kRW contiguous ranges, one per wavefront.  A
-// wavefront loads the x fragments of RS slices at once (one trip to HBM
-// per round) and streams W_g, which every workgroup reads and so stays in
-// L2, through a ring of RD slices in registers; each W_g value is split
+// wavefront loads the x fragments of up to RS slices at once (one trip to
+// HBM per round) and streams W_g, which every workgroup reads and so stays
+// in L2, through a ring of RD slices in registers; each W_g value is split
 // once for all MBLK token blocks.  The partial logit tiles are summed in
 // LDS in wavefront order (deterministic), then each wavefront selects for
 // four tokens at a time.
+//
+// Small batches split K over KS workgroups per token block as well
+// (blockIdx.y); each then writes its summed tile to partial[ks][t][e] and
+// router_select_kernel finishes the sum in ks order and selects.
 template <int MBLK, int NBLK>
 __global__ __launch_bounds__(kRW * kWave) void router_mfma_kernel(
     const bf16_t* __restrict__ x, const float* __restrict__ wg, const float* __restrict__ bias,
     int T, int d, int Nr, int K, int gate, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w) {
+    float* __restrict__ topk_w, int KS, float* __restrict__ partial) {
   constexpr int TB = 32 * MBLK;
   constexpr int NPAD = 32 * NBLK;
   // Selection: groups of 16 lanes, one token each (4-step reductions).
@@ -303,34 +335,17 @@ __global__ __launch_bounds__(kRW * kWave) void router_mfma_kernel(
       for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.0f;
 
   const int S = d / 16;
-  const int s0 = wave * S / kRW, s1 = (wave + 1) * S / kRW;
-  // Branch-free rounds (so every wait on a load is an exact count): slices
-  // past the end of the range re-read the last slice and multiply zeros.
-  for (int rs = s0; rs < s1; rs += RS) {
-    const int last = min(RS, s1 - rs) - 1;
-    bf16x8 xa[RS][MBLK];
-#pragma unroll
-    for (int i = 0; i < RS; ++i)
-#pragma unroll
-      for (int mb = 0; mb < MBLK; ++mb)
-        xa[i][mb] = *reinterpret_cast<const bf16x8*>(xp[mb] + (rs + min(i, last)) * 16);
-    float4 wr[RD][NBLK][2];
-#pragma unroll
-    for (int i = 0; i < RD; ++i) load_w_slice<NBLK>(wr[i], wp, (rs + min(i, last)) * 16);
-    // Keep every load above at the top: the scheduler would otherwise sink
-    // them next to their first use and serialise the round trips.
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < RS; ++i) {
-      if (i > last) {
-#pragma unroll
-        for (int mb = 0; mb < MBLK; ++mb) xa[i][mb] = bf16x8{};
-      }
-      router_mma<MBLK, NBLK>(acc, xa[i], wr[i % RD], ev);
-      if (i + RD < RS) load_w_slice<NBLK>(wr[i % RD], wp, (rs + min(i + RD, last)) * 16);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  const int range = blockIdx.y * kRW + wave, nranges = KS * kRW;
+  const int s0 = range * S / nranges, s1 = (range + 1) * S / nranges;
+  // Full rounds of RS slices, then the remainder in rounds of 8, 4, 2, 1.
+  int rs = s0;
+  for (; rs + RS <= s1; rs += RS) router_round<RS, RD, MBLK, NBLK>(acc, xp, wp, ev, rs);
+  if constexpr (RS > 8) {
+    if (rs + 8 <= s1) { router_round<8, RD, MBLK, NBLK>(acc, xp, wp, ev, rs); rs += 8; }
   }
+  if (rs + 4 <= s1) { router_round<4, RD, MBLK, NBLK>(acc, xp, wp, ev, rs); rs += 4; }
+  if (rs + 2 <= s1) { router_round<2, RD, MBLK, NBLK>(acc, xp, wp, ev, rs); rs += 2; }
+  if (rs + 1 <= s1) router_round<1, RD, MBLK, NBLK>(acc, xp, wp, ev, rs);
 
   // D[row][col] of a 32x32 block: lane (col + 32*h), register v, row 8*(v/4) + 4*h + v%4.
   for (int w = 0; w < kRW; ++w) {
@@ -347,6 +362,15 @@ __global__ __launch_bounds__(kRW * kWave) void router_mfma_kernel(
           }
     }
     __syncthreads();
+  }
+
+  if (KS > 1) {
+    for (int i = threadIdx.x; i < TB * NPAD; i += kRW * kWave) {
+      const int tl = i / NPAD, c = i % NPAD;
+      const int64_t t = tok0 + tl;
+      if (t < T) partial[(static_cast<int64_t>(blockIdx.y) * T + t) * NPAD + c] = lg[tl][c];
+    }
+    return;
   }
 
   const int grp = lane / NP;
@@ -370,13 +394,48 @@ __global__ __launch_bounds__(kRW * kWave) void router_mfma_kernel(
   }
 }
 
+// Sum of the KS partial logit tiles (in ks order) and selection: one
+// wavefront per four tokens, 16 lanes per token.
+template <int NBLK>
+__global__ __launch_bounds__(kWave) void router_select_kernel(
+    const float* __restrict__ partial, const float* __restrict__ bias, int T, int Nr, int K,
+    int gate, int KS, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+  constexpr int NPAD = 32 * NBLK;
+  constexpr int NP = 16;
+  constexpr int EPL = NPAD / NP;
+  const int lane = threadIdx.x;
+  const int grp = lane / NP;
+  const int gl = lane % NP;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * (kWave / NP) + grp;
+  if (t >= T) return;  // uniform within the group
+  int e[EPL];
+  bool evq[EPL];
+  float z[EPL];
+#pragma unroll
+  for (int q = 0; q < EPL; ++q) {
+    e[q] = gl + NP * q;
+    evq[q] = e[q] < Nr;
+    float acc = 0.0f;
+    for (int ks = 0; ks < KS; ++ks) acc += partial[(static_cast<int64_t>(ks) * T + t) * NPAD + e[q]];
+    z[q] = evq[q] ? acc + (bias != nullptr ? bias[e[q]] : 0.0f) : -INFINITY;
+  }
+  select_and_store<NP, EPL>(z, e, evq, t, K, gate, grp, lane, topk_idx, topk_w);
+}
+
 template <int MBLK, int NBLK>
 hipError_t launch_mfma(const RouteArgs& a, hipStream_t s) {
   constexpr int TB = 32 * MBLK;
-  const int grid = (a.T + TB - 1) / TB;
-  hipLaunchKernelGGL((router_mfma_kernel<MBLK, NBLK>), dim3(grid), dim3(kRW * kWave), 0, s,
+  const int blocks = (a.T + TB - 1) / TB;
+  // Split K when the token blocks alone would leave most CUs idle.
+  const int KS = (a.partial != nullptr && MBLK == 1) ? max(1, min(kRouterSplit, 128 / blocks)) : 1;
+  hipLaunchKernelGGL((router_mfma_kernel<MBLK, NBLK>), dim3(blocks, KS), dim3(kRW * kWave), 0, s,
                      static_cast<const bf16_t*>(a.x), a.w_router, a.bias, a.T, a.d, a.n_routed,
-                     a.top_k, a.gate, a.topk_idx, a.topk_w);
+                     a.top_k, a.gate, a.topk_idx, a.topk_w, KS, a.partial);
+  if (KS == 1) return hipGetLastError();
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((router_select_kernel<NBLK>), dim3((a.T + 3) / 4), dim3(kWave), 0, s,
+                     a.partial, a.bias, a.T, a.n_routed, a.top_k, a.gate, KS, a.topk_idx, a.topk_w);
   return hipGetLastError();
 }
 
