@@ -426,43 +426,56 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
   }
 #undef MOE_K_LOOP
 
-  // ---- epilogue: D[row][col] of a 32x32 block sits in lane (col + 32*h),
-  //      register v, row = 8*(v/4) + 4*h + v%4.
-  bf16_t* C = static_cast<bf16_t*>(p.C);
+  // ---- epilogue: the bf16 tile goes through LDS (the stage buffers are
+  //      free now) so that global stores are whole 16-byte chunks of rows.
+  //      D[row][col] of a 32x32 block sits in lane (col + 32*h), register v,
+  //      row = 8*(v/4) + 4*h + v%4.
+  //      In LDS, 16-byte chunk k of tile row r sits at chunk k ^ (r & 7), so
+  //      both the 2-byte writes and the 16-byte reads spread over the banks.
+  constexpr int NT = WM * WN * kWave;
+  static_assert(OUT_N % 64 == 0 && BM * OUT_N <= STAGES * SE, "C tile does not fit the stages");
+  __syncthreads();  // every wavefront is done reading the last stage
+  bf16_t* ct = smem;
+  auto cpos = [](int r, int c) { return r * OUT_N + ((((c >> 3) ^ (r & 7))) << 3) + (c & 7); };
   const int col_in = lane & 31;
   const int hrow = (lane >> 5) * 4;
   if (MODE == kGateUp) {
     constexpr int half = NB / 2;
 #pragma unroll
-    for (int i = 0; i < MB; ++i) {
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
       for (int j = 0; j < half; ++j) {
-        const int col = nt * OUT_N + wn * (TN / 2) + j * 32 + col_in;
-        if (col >= p.N) continue;
+        const int c = wn * (TN / 2) + j * 32 + col_in;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int r = wm * TM + i * 32 + 8 * (v >> 2) + hrow + (v & 3);
-          if (r < rows) {
-            const float gv = acc[i][j][v], uv = acc[i][j + half][v];
-            C[(row0 + r) * p.ldc + col] = f32_to_bf16(silu_fast(gv) * uv);
-          }
+          ct[cpos(r, c)] = f32_to_bf16(silu_fast(acc[i][j][v]) * acc[i][j + half][v]);
         }
       }
-    }
   } else {
 #pragma unroll
-    for (int i = 0; i < MB; ++i) {
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const int col = nt * OUT_N + wn * TN + j * 32 + col_in;
-        if (col >= p.N) continue;
+        const int c = wn * TN + j * 32 + col_in;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int r = wm * TM + i * 32 + 8 * (v >> 2) + hrow + (v & 3);
-          if (r < rows) C[(row0 + r) * p.ldc + col] = f32_to_bf16(acc[i][j][v]);
+          ct[cpos(r, c)] = f32_to_bf16(acc[i][j][v]);
         }
       }
-    }
+  }
+  __syncthreads();
+  // Rows past the tile's end and columns past N (N is a multiple of 8) are
+  // not stored.
+  constexpr int CPR = OUT_N / 8;  // 16-byte chunks per tile row
+  bf16_t* C = static_cast<bf16_t*>(p.C);
+  const int col0 = nt * OUT_N;
+  for (int idx = tid; idx < rows * CPR; idx += NT) {
+    const int r = idx / CPR, c8 = (idx % CPR) * 8;
+    if (col0 + c8 < p.N)
+      *reinterpret_cast<uint4*>(C + (row0 + r) * p.ldc + col0 + c8) =
+          *reinterpret_cast<const uint4*>(ct + cpos(r, c8));
   }
 #endif
 }
