@@ -514,6 +514,9 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
   const int64_t mean_rows = a.rows_total / (a.offsets ? a.n_groups + a.n_extra : 1);
   if (mean_rows >= 192) return launch_cfg<256, 256, 2, 4, 64, 2>(a, s);
   if (mean_rows >= 64) return launch_cfg<128, 256, 2, 2, 64, 2>(a, s);
+  // Few rows per group: the weights stream through.  Down projections (the
+  // shorter K) use narrower tiles so that more of them run at once.
+  if (a.mode == kDown) return launch_cfg<32, 128, 1, 2, 64, 2>(a, s);
   return launch_cfg<32, 256, 1, 4, 64, 2>(a, s);
 }
 
