@@ -278,6 +278,10 @@ int moe_workspace_size(const moe_layer* layer, int64_t T, size_t* bytes) {
   return MOE_OK;
 }
 
+static moe::RouteArgs route_args(const moe_layer* layer, int64_t T, const void* x,
+                                 const float* w_router, const float* logit_bias, int32_t* topk_idx,
+                                 float* topk_w, float* partial);
+
 static int route_impl(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
                       const float* logit_bias, int32_t* topk_idx, float* topk_w, float* partial,
                       void* stream) {
@@ -288,6 +292,14 @@ static int route_impl(const moe_layer* layer, int64_t T, const void* x, const fl
   MOE_TRY(needT(topk_idx, T));
   MOE_TRY(needT(topk_w, T));
   if (T == 0) return MOE_OK;
+  MOE_HIP(moe::launch_route(route_args(layer, T, x, w_router, logit_bias, topk_idx, topk_w, partial),
+                            static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+static moe::RouteArgs route_args(const moe_layer* layer, int64_t T, const void* x,
+                                 const float* w_router, const float* logit_bias, int32_t* topk_idx,
+                                 float* topk_w, float* partial) {
   moe::RouteArgs a{};
   a.partial = partial;
   a.x = x;
@@ -301,8 +313,7 @@ static int route_impl(const moe_layer* layer, int64_t T, const void* x, const fl
   a.x_bf16 = layer->dtype == MOE_BF16;
   a.topk_idx = topk_idx;
   a.topk_w = topk_w;
-  MOE_HIP(moe::launch_route(a, static_cast<hipStream_t>(stream)));
-  return MOE_OK;
+  return a;
 }
 
 int moe_route(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
@@ -310,10 +321,10 @@ int moe_route(const moe_layer* layer, int64_t T, const void* x, const float* w_r
   return route_impl(layer, T, x, w_router, logit_bias, topk_idx, topk_w, nullptr, stream);
 }
 
-static int permute_impl(const moe_layer* layer, int64_t T, const int32_t* topk_idx,
-                        const void* x, int32_t* counts, int32_t* offsets, int32_t* row_token,
-                        int32_t* slot_row, void* x_perm, void* ws, const Layout& lo,
-                        hipStream_t s) {
+static moe::PermuteArgs permute_args(const moe_layer* layer, int64_t T, const int32_t* topk_idx,
+                                     const void* x, int32_t* counts, int32_t* offsets,
+                                     int32_t* row_token, int32_t* slot_row, void* x_perm, void* ws,
+                                     const Layout& lo) {
   moe::PermuteArgs a{};
   a.topk_idx = topk_idx;
   a.x = x;
@@ -330,7 +341,16 @@ static int permute_impl(const moe_layer* layer, int64_t T, const int32_t* topk_i
   a.block_counts = reinterpret_cast<int32_t*>(at(ws, lo.block_counts));
   a.block_base = reinterpret_cast<int32_t*>(at(ws, lo.block_base));
   a.local_rank = reinterpret_cast<int32_t*>(at(ws, lo.local_rank));
-  MOE_HIP(moe::launch_permute(a, s));
+  return a;
+}
+
+static int permute_impl(const moe_layer* layer, int64_t T, const int32_t* topk_idx,
+                        const void* x, int32_t* counts, int32_t* offsets, int32_t* row_token,
+                        int32_t* slot_row, void* x_perm, void* ws, const Layout& lo,
+                        hipStream_t s) {
+  MOE_HIP(moe::launch_permute(permute_args(layer, T, topk_idx, x, counts, offsets, row_token,
+                                           slot_row, x_perm, ws, lo),
+                              s));
   return MOE_OK;
 }
 
@@ -469,14 +489,16 @@ static int forward_impl(const moe_layer* layer, int64_t T, const void* x,
   void* h_shared = at(ws, lo.h_shared);
   void* y_shared = layer->n_shared > 0 ? at(ws, lo.y_shared) : nullptr;
 
-  MOE_TRY(m.mark(0));
   // With the workspace at hand, small batches may split the router's K.
-  MOE_TRY(route_impl(layer, T, x, w_router, logit_bias, topk_idx, topk_w,
-                     reinterpret_cast<float*>(at(ws, lo.router_part)), stream));
+  const moe::RouteArgs ra = route_args(layer, T, x, w_router, logit_bias, topk_idx, topk_w,
+                                       reinterpret_cast<float*>(at(ws, lo.router_part)));
+  const moe::PermuteArgs pa = permute_args(layer, T, topk_idx, nullptr, counts, offsets, row_token,
+                                           slot_row, nullptr, ws, lo);
+  MOE_TRY(m.mark(0));
+  MOE_HIP(moe::launch_route(ra, s));
   MOE_TRY(m.mark(1));
   MOE_TRY(m.mark(2));
-  MOE_TRY(permute_impl(layer, T, topk_idx, nullptr, counts, offsets, row_token, slot_row,
-                       nullptr, ws, lo, s));
+  MOE_HIP(moe::launch_permute(pa, s));
   MOE_TRY(m.mark(3));
   // Routed experts; the gather x[row_token[r]] happens inside the A-tile load.
   moe::GemmArgs gu = routed_gate_up(layer, T, offsets, x, row_token, w_gate, w_up, H);

@@ -15,6 +15,7 @@
 //           slot_row and, when asked, copies x rows into x_perm (one wave per
 //           token reads the row once and writes it K' times, 16 B per lane).
 #include "common.h"
+#include "dispatch_small.h"
 #include "kernels.h"
 
 namespace moe {
@@ -179,98 +180,12 @@ __global__ __launch_bounds__(256) void scatter_copy_kernel(
 }
 
 // Small batches (T <= kSmallTokens, no row copy): the three steps above in
-// one workgroup, one thread per token.  Ballots give per-wave counts and
-// in-wave ranks as in count_kernel; the scan runs over experts in LDS; a
-// row is offsets[e] + rows of e in earlier waves + rank in the wave, which
-// is the same stable order.
-constexpr int kSmallTokens = 1024;
-
+// one workgroup, one thread per token (small_dispatch, dispatch_small.h).
 __global__ __launch_bounds__(kSmallTokens) void dispatch_small_kernel(
     const int32_t* __restrict__ idx, int T, int K, int Nr, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ row_token, int32_t* __restrict__ slot_row) {
-  constexpr int NWV = kSmallTokens / kWave;
-  __shared__ uint64_t masks[NWV][kMaxExperts];
-  __shared__ int cnt[NWV][kMaxExperts];
-  __shared__ int offs[kMaxExperts + 1];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int t = threadIdx.x;
-  const bool valid = t < T;
-  int ids[kMaxK];
-  uint64_t bits0 = 0, bits1 = 0, bits2 = 0, bits3 = 0;
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    ids[j] = -1;
-    if (j < K && valid) {
-      const int e = idx[static_cast<int64_t>(t) * K + j];
-      ids[j] = e;
-      const uint64_t b = 1ull << (e & 63);
-      const int w = e >> 6;
-      bits0 |= (w == 0) ? b : 0ull;
-      bits1 |= (w == 1) ? b : 0ull;
-      bits2 |= (w == 2) ? b : 0ull;
-      bits3 |= (w == 3) ? b : 0ull;
-    }
-  }
-  for (int e = 0; e < Nr; ++e) {
-    const int w = e >> 6;
-    const uint64_t bits = (w == 0) ? bits0 : (w == 1) ? bits1 : (w == 2) ? bits2 : bits3;
-    const uint64_t m = __ballot((bits >> (e & 63)) & 1ull);
-    if (lane == 0) {
-      masks[wave][e] = m;
-      cnt[wave][e] = __popcll(m);
-    }
-  }
-  __syncthreads();
-  // Per-expert totals in parallel, then an exclusive scan over the experts
-  // in wavefront 0 (four experts per lane, shuffle prefix sums).
-  if (threadIdx.x < Nr) {
-    int c = 0;
-#pragma unroll
-    for (int w = 0; w < NWV; ++w) c += cnt[w][threadIdx.x];
-    offs[threadIdx.x + 1] = c;
-  }
-  __syncthreads();
-  if (wave == 0) {
-    int v[4], sum = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane * 4 + q;
-      v[q] = e < Nr ? offs[e + 1] : 0;
-      sum += v[q];
-    }
-    int incl = sum;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int u = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += u;
-    }
-    int run = incl - sum;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane * 4 + q;
-      if (e < Nr) offs[e] = run;
-      run += v[q];
-    }
-    if (lane == kWave - 1) offs[Nr] = incl;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e <= Nr; e += kSmallTokens) {
-    offsets[e] = offs[e];
-    if (e < Nr) counts[e] = offs[e + 1] - offs[e];
-  }
-  if (!valid) return;
-  const uint64_t below = (1ull << lane) - 1ull;
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    if (j < K) {
-      const int e = ids[j];
-      int r = offs[e] + __popcll(masks[wave][e] & below);
-      for (int w = 0; w < wave; ++w) r += cnt[w][e];
-      slot_row[static_cast<int64_t>(t) * K + j] = r;
-      row_token[r] = t;
-    }
-  }
+  __shared__ SmallDispatchLds sh;
+  small_dispatch(idx, T, K, Nr, counts, offsets, row_token, slot_row, sh);
 }
 
 }  // namespace

@@ -1,0 +1,111 @@
+// Dispatch of a small batch inside one workgroup of kSmallTokens threads
+// (the single-workgroup path of dispatch.hip).
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+constexpr int kSmallTokens = 1024;
+constexpr int kDispatchMaxK = 16;
+constexpr int kDispatchMaxExperts = 256;
+
+// Stable counting sort of the T*K assignments of topk_idx (T <= kSmallTokens)
+// by expert, one thread per token: ballots give per-wave counts and in-wave
+// ranks; the scan runs over experts in LDS; a row is offsets[e] + rows of e
+// in earlier waves + rank in the wave, i.e. ascending token order.  Every
+// thread of the workgroup must call it.
+struct SmallDispatchLds {
+  uint64_t masks[kSmallTokens / kWave][kDispatchMaxExperts];
+  int cnt[kSmallTokens / kWave][kDispatchMaxExperts];
+  int offs[kDispatchMaxExperts + 1];
+};
+
+__device__ __forceinline__ void small_dispatch(const int32_t* __restrict__ idx, int T, int K, int Nr,
+                                               int32_t* __restrict__ counts,
+                                               int32_t* __restrict__ offsets,
+                                               int32_t* __restrict__ row_token,
+                                               int32_t* __restrict__ slot_row, SmallDispatchLds& sh) {
+  constexpr int NWV = kSmallTokens / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int t = threadIdx.x;
+  const bool valid = t < T;
+  int ids[kDispatchMaxK];
+  uint64_t bits0 = 0, bits1 = 0, bits2 = 0, bits3 = 0;
+#pragma unroll
+  for (int j = 0; j < kDispatchMaxK; ++j) {
+    ids[j] = -1;
+    if (j < K && valid) {
+      const int e = idx[static_cast<int64_t>(t) * K + j];
+      ids[j] = e;
+      const uint64_t b = 1ull << (e & 63);
+      const int w = e >> 6;
+      bits0 |= (w == 0) ? b : 0ull;
+      bits1 |= (w == 1) ? b : 0ull;
+      bits2 |= (w == 2) ? b : 0ull;
+      bits3 |= (w == 3) ? b : 0ull;
+    }
+  }
+  for (int e = 0; e < Nr; ++e) {
+    const int w = e >> 6;
+    const uint64_t bits = (w == 0) ? bits0 : (w == 1) ? bits1 : (w == 2) ? bits2 : bits3;
+    const uint64_t m = __ballot((bits >> (e & 63)) & 1ull);
+    if (lane == 0) {
+      sh.masks[wave][e] = m;
+      sh.cnt[wave][e] = __popcll(m);
+    }
+  }
+  __syncthreads();
+  // Per-expert totals in parallel, then an exclusive scan over the experts
+  // in wavefront 0 (four experts per lane, shuffle prefix sums).
+  if (threadIdx.x < Nr) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) c += sh.cnt[w][threadIdx.x];
+    sh.offs[threadIdx.x + 1] = c;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    int v[4], sum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane * 4 + q;
+      v[q] = e < Nr ? sh.offs[e + 1] : 0;
+      sum += v[q];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int u = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += u;
+    }
+    int run = incl - sum;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane * 4 + q;
+      if (e < Nr) sh.offs[e] = run;
+      run += v[q];
+    }
+    if (lane == kWave - 1) sh.offs[Nr] = incl;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e <= Nr; e += kSmallTokens) {
+    offsets[e] = sh.offs[e];
+    if (e < Nr) counts[e] = sh.offs[e + 1] - sh.offs[e];
+  }
+  if (!valid) return;
+  const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int j = 0; j < kDispatchMaxK; ++j) {
+    if (j < K) {
+      const int e = ids[j];
+      int r = sh.offs[e] + __popcll(sh.masks[wave][e] & below);
+      for (int w = 0; w < wave; ++w) r += sh.cnt[w][e];
+      slot_row[static_cast<int64_t>(t) * K + j] = r;
+      row_token[r] = t;
+    }
+  }
+}
+
+}  // namespace moe

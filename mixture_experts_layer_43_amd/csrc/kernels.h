@@ -42,6 +42,7 @@ struct PermuteArgs {
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
 
+
 // ---- grouped GEMMs (gemm_bf16.hip, gemm_f32.hip) ----
 enum GemmMode { kGateUp = 0, kDown = 1 };
 

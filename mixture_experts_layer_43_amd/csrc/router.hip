@@ -394,6 +394,22 @@ __global__ __launch_bounds__(kRW * kWave) void router_mfma_kernel(
   }
 }
 
+// Logit (t, e) as the sum of the KS <= kRouterSplit partial tiles, in ks
+// order; all loads are issued before the first add.
+template <int NPAD>
+__device__ __forceinline__ float sum_partials(const float* __restrict__ partial, int KS, int T,
+                                              int64_t t, int e) {
+  float v[kRouterSplit];
+#pragma unroll
+  for (int ks = 0; ks < kRouterSplit; ++ks)
+    v[ks] = partial[(static_cast<int64_t>(min(ks, KS - 1)) * T + t) * NPAD + e];
+  float acc = 0.0f;
+#pragma unroll
+  for (int ks = 0; ks < kRouterSplit; ++ks)
+    if (ks < KS) acc += v[ks];
+  return acc;
+}
+
 // Sum of the KS partial logit tiles (in ks order) and selection: one
 // wavefront per four tokens, 16 lanes per token.
 template <int NBLK>
@@ -415,9 +431,8 @@ __global__ __launch_bounds__(kWave) void router_select_kernel(
   for (int q = 0; q < EPL; ++q) {
     e[q] = gl + NP * q;
     evq[q] = e[q] < Nr;
-    float acc = 0.0f;
-    for (int ks = 0; ks < KS; ++ks) acc += partial[(static_cast<int64_t>(ks) * T + t) * NPAD + e[q]];
-    z[q] = evq[q] ? acc + (bias != nullptr ? bias[e[q]] : 0.0f) : -INFINITY;
+    z[q] = sum_partials<NPAD>(partial, KS, T, t, e[q]);
+    z[q] = evq[q] ? z[q] + (bias != nullptr ? bias[e[q]] : 0.0f) : -INFINITY;
   }
   select_and_store<NP, EPL>(z, e, evq, t, K, gate, grp, lane, topk_idx, topk_w);
 }
