@@ -271,3 +271,44 @@ def test_repeat_calls_are_deterministic():
     a = host(run_forward(cfg, d).y)
     b = host(run_forward(cfg, d).y)
     np.testing.assert_array_equal(a, b)
+
+
+def test_forward_timed_matches_forward():
+    """moe_forward_timed with only some markers set computes exactly what
+    moe_forward computes, and every set marker pair brackets a stage."""
+    import ctypes
+    from mixture_experts_layer_43_amd import _lib
+    cfg, inp, ref = case("16b-decode")
+    announce("forward_timed markers")
+    d = upload(inp)
+    f = run_forward(cfg, d)
+    y0 = f.y.clone()
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    nev = 2 * _lib.MOE_NUM_STAGES
+    arr = (ctypes.c_void_p * nev)()
+    marked = [_lib.STAGES.index("route"), _lib.STAGES.index("routed_gate_up")]
+    for st in marked:
+        for i in (2 * st, 2 * st + 1):
+            ev = ctypes.c_void_p()
+            assert hip.hipEventCreate(ctypes.byref(ev)) == 0
+            arr[i] = ev.value
+    p = ops._p
+    f.y.zero_()
+    _lib.check("moe_forward_timed", _lib.lib().moe_forward_timed(
+        ctypes.byref(ops.Layer.of(cfg).c()), cfg.tokens, p(d["x"]), p(d["w_router"]), p(d["bias"]),
+        p(d["w_gate"]), p(d["w_up"]), p(d["w_down"]), p(d["ws_gate"]), p(d["ws_up"]), p(d["ws_down"]),
+        None, p(f.y), p(f.topk_idx), p(f.topk_w), p(f.counts), p(f.offsets), p(f.ws), f.ws.numel(),
+        ops._stream(), arr))
+    torch.cuda.synchronize()
+    assert torch.equal(f.y, y0)
+    t = ctypes.c_float()
+    for st in marked:
+        assert hip.hipEventElapsedTime(ctypes.byref(t), arr[2 * st], arr[2 * st + 1]) == 0
+        assert t.value > 0.0
+    for i in range(nev):
+        if arr[i]:
+            hip.hipEventDestroy(arr[i])
+    check_routing(f, ref)
