@@ -5,7 +5,8 @@ and the CPU-baseline leg of bench.py may import anything from this package.
 The HIP library never calls into it and it never calls into the HIP library;
 the two share nothing except the seeded inputs from `synth`.
 
-Every function is pinned by tests/test_oracle_pins.py against closed forms,
+Every function is pinned by tests/test_oracle_pins.py (the layer) and
+tests/test_oracle_stats_pins.py (routing statistics) against closed forms,
 special cases and a pure-Python brute force (see tests/_brute.py).
 """
 from .moe import (  # noqa: F401
@@ -22,3 +23,4 @@ from .moe import (  # noqa: F401
     softmax,
 )
 from .gap import enforce_gap, topk_gap  # noqa: F401
+from .stats import routing_stats  # noqa: F401
