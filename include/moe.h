@@ -103,6 +103,34 @@ int moe_workspace_size(const moe_layer* layer, int64_t T, size_t* bytes);
 int moe_route(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
               const float* logit_bias, int32_t* topk_idx, float* topk_w, void* stream);
 
+/* Floats written to `stats` by moe_route_stats for N_r experts, D groups. */
+#define MOE_STATS_LEN(n_routed, n_devices) (2 * (n_routed) + 2 * (n_devices) + 3)
+
+/* moe_route plus the routing statistics of the batch, for training: the
+ * balance terms of the DeepSeekMoE page, section 3.3 (eq. 12-14 expert
+ * level, eq. 15-17 device level) and the router z-loss of the MoE-survey
+ * blog page, section 5.  topk_idx and topk_w are bit-identical to
+ * moe_route's.  stats [MOE_STATS_LEN(N_r, D)] fp32, device pointer:
+ *   [0, N_r)             P_i = (1/T) sum_t s_{i,t}, s_t = Softmax over the N_r
+ *                        routed experts of the logits incl. logit_bias (for
+ *                        both gate kinds)
+ *   [N_r, 2 N_r)         f_i = N_r / (K' T) * #{t : i among t's top-K'}
+ *   [2 N_r, +D)          f'_g = mean of f_i over group g, the experts
+ *                        [g N_r/D, (g+1) N_r/D)
+ *   [2 N_r + D, +D)      P'_g = sum of P_i over group g
+ *   [2 N_r + 2D]         L_ExpBal = sum_i f_i P_i        (alpha_1 = 1)
+ *   [2 N_r + 2D + 1]     L_DevBal = sum_g f'_g P'_g      (alpha_2 = 1)
+ *   [2 N_r + 2D + 2]     z-loss = (1/T) sum_t lse_t^2
+ * lse [T] fp32 or NULL: lse_t = log sum_i exp z_{t,i} over the routed
+ * experts.  With K' = 1, L_ExpBal is the Switch balance loss (MoE-survey
+ * blog page, section 4) at alpha = 1.  n_devices = D must divide N_r
+ * (else MOE_ERR_INVALID_ARG).  Sums run in fp64 in a fixed order, so
+ * repeated calls return identical bits.  T == 0 writes zeros. */
+int moe_route_stats(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
+                    const float* logit_bias, int32_t n_devices, int32_t* topk_idx,
+                    float* topk_w, float* stats, float* lse, void* ws, size_t ws_bytes,
+                    void* stream);
+
 /* Dispatch: stable counting sort of the T*K' (token, expert) assignments by
  * expert (the per-expert token lists that let only chosen experts run).
  *   topk_idx [T, K'] with 0 <= id < N_r and distinct ids per token (other

@@ -5,4 +5,6 @@ ABI in include/moe.h; this package only marshals torch tensors to it.
 """
 from . import ops  # noqa: F401
 from ._lib import LIB_PATH, MoeError, lib  # noqa: F401
-from .ops import Forward, Layer, combine, expert_ffn, forward, permute, route, shared_ffn  # noqa: F401
+from .ops import (  # noqa: F401
+    Forward, Layer, combine, expert_ffn, forward, permute, route, route_stats, shared_ffn, split_stats,
+)

@@ -17,7 +17,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t router_part, block_counts, block_base, local_rank, topk_idx, topk_w, counts, offsets, row_token,
+  size_t router_part, stats_part, block_counts, block_base, local_rank, topk_idx, topk_w, counts, offsets, row_token,
       slot_row, h, y_perm, h_shared, y_shared, total;
 };
 
@@ -46,6 +46,7 @@ Layout layout_of(const moe_layer* L, int64_t T) {
     return at;
   };
   o.router_part = take(moe::router_partial_bytes(T));
+  o.stats_part = take(moe::route_stats_bytes(T));
   o.block_counts = take(NB * Nr * 4);
   o.block_base = take(NB * Nr * 4);
   o.local_rank = take(P * 4);
@@ -319,6 +320,28 @@ static moe::RouteArgs route_args(const moe_layer* layer, int64_t T, const void* 
 int moe_route(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
               const float* logit_bias, int32_t* topk_idx, float* topk_w, void* stream) {
   return route_impl(layer, T, x, w_router, logit_bias, topk_idx, topk_w, nullptr, stream);
+}
+
+int moe_route_stats(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
+                    const float* logit_bias, int32_t n_devices, int32_t* topk_idx, float* topk_w,
+                    float* stats, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_layer(layer, T));
+  MOE_TRY(needT(x, T));
+  MOE_TRY(need(w_router));
+  MOE_TRY(opt(logit_bias));
+  MOE_TRY(needT(topk_idx, T));
+  MOE_TRY(needT(topk_w, T));
+  MOE_TRY(need(stats));
+  MOE_TRY(opt(lse));
+  if (n_devices < 1 || layer->n_routed % n_devices != 0) return MOE_ERR_INVALID_ARG;
+  const Layout lo = layout_of(layer, T);
+  MOE_TRY(need(ws));
+  if (ws_bytes < lo.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  moe::RouteArgs a = route_args(layer, T, x, w_router, logit_bias, topk_idx, topk_w, nullptr);
+  a.stats_part = reinterpret_cast<double*>(at(ws, lo.stats_part));
+  a.lse = lse;
+  MOE_HIP(moe::launch_route_stats(a, n_devices, stats, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
 }
 
 static moe::PermuteArgs permute_args(const moe_layer* layer, int64_t T, const int32_t* topk_idx,

@@ -16,6 +16,8 @@ struct RouteArgs {
   int32_t* topk_idx;       // [T, K']
   float* topk_w;           // [T, K']
   float* partial;          // null, or scratch of router_partial_bytes(T) for split-K logits
+  double* stats_part;      // null, or scratch of route_stats_bytes(T): routing statistics on
+  float* lse;              // [T] or null: per-token log-sum-exp (statistics only)
 };
 // Split-K of the matrix-core router for small batches: at most this many
 // K slices, each writing a [T, 128] fp32 partial tile.
@@ -24,6 +26,19 @@ inline size_t router_partial_bytes(int64_t T) {
   return T < 4096 ? static_cast<size_t>(kRouterSplit) * static_cast<size_t>(T) * 128 * 4 : 0;
 }
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+
+// Routing statistics: every router workgroup (at least 32 tokens each) sums
+// its tokens' softmax values, choices and squared log-sum-exps into one row
+// of kStatsStride doubles; route_stats_kernel folds the rows in order.
+constexpr int kStatsCount = 256;   // offset of the choice counts in a row
+constexpr int kStatsZ = 512;       // offset of the sum of lse^2
+constexpr int kStatsStride = 514;
+inline size_t route_stats_bytes(int64_t T) {
+  return static_cast<size_t>((T + 31) / 32) * kStatsStride * sizeof(double);
+}
+// Router (a.stats_part set, a.partial null) followed by the fold into
+// stats[2 N_r + 2 D + 3] (layout in include/moe.h, moe_route_stats).
+hipError_t launch_route_stats(const RouteArgs& a, int n_devices, float* stats, hipStream_t s);
 
 // ---- dispatch (dispatch.hip) ----
 constexpr int kCountBlock = 256;  // tokens per counting block

@@ -45,17 +45,37 @@ __device__ __forceinline__ void load4<bf16_t>(const bf16_t* p, float (&v)[4]) {
   v[3] = __uint_as_float(q.y & 0xFFFF0000u);
 }
 
+// Running sums of the routing statistics (DeepSeekMoE page, section 3.3,
+// eq. 13-14; MoE-survey blog page, section 5, z-loss) over the tokens one
+// lane's group has selected for: s_i and times chosen for each expert the
+// lane owns, and the squared log-sum-exp (the same on every lane of a group).
+template <int EPL>
+struct StatAcc {
+  double p[EPL];
+  int c[EPL];
+  double z2;
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) { p[q] = 0.0; c[q] = 0; }
+    z2 = 0.0;
+  }
+};
+
 // Top-K' of one token's logits z (lane-per-expert inside a group of NP
 // lanes, EPL experts per lane: expert e[q] = lane-in-group + NP*q), gate
 // values, and the ascending-id store.  K' rounds of group arg-max, ties to
 // the lower id; softmax over all routed experts (gate 0) or over the chosen
-// ones (gate 1), both relative to the largest logit.
-template <int NP, int EPL>
+// ones (gate 1), both relative to the largest logit.  STATS: also adds the
+// token's full softmax s (both gates), its choices and lse^2 to sa, and
+// writes lse[t] when lse is set.
+template <int NP, int EPL, bool STATS = false>
 __device__ __forceinline__ void select_and_store(const float (&z)[EPL], const int (&e)[EPL],
                                                  const bool (&ev)[EPL], int64_t t, int K,
                                                  int gate, int grp, int lane,
                                                  int32_t* __restrict__ topk_idx,
-                                                 float* __restrict__ topk_w) {
+                                                 float* __restrict__ topk_w,
+                                                 StatAcc<EPL>* sa = nullptr,
+                                                 float* __restrict__ lse = nullptr) {
   bool sel[EPL];
 #pragma unroll
   for (int q = 0; q < EPL; ++q) sel[q] = false;
@@ -97,13 +117,66 @@ __device__ __forceinline__ void select_and_store(const float (&z)[EPL], const in
     }
     prior += __popcll(m);
   }
+  if constexpr (STATS) {
+    float full = denom;
+    if (gate != 0) {
+      float pf = 0.0f;
+#pragma unroll
+      for (int q = 0; q < EPL; ++q) pf += ex[q];
+      full = group_sum<NP>(pf);
+    }
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) {
+      sa->p[q] += static_cast<double>(ex[q] / full);
+      sa->c[q] += sel[q] ? 1 : 0;
+    }
+    const double l = static_cast<double>(zmax) + log(static_cast<double>(full));
+    sa->z2 += l * l;
+    if (lse != nullptr && (lane % NP) == 0) lse[t] = static_cast<float>(l);
+  }
 }
 
-template <typename XT, int NP, int EPL>
+// Sum of the lanes' StatAcc over one workgroup of W wavefronts in a fixed
+// order (xor shuffles across the groups of a wavefront, then the wavefronts
+// in order) into row[0, NP*EPL) (sum of s per expert), row[kStatsCount + e]
+// (times chosen) and row[kStatsZ] (sum of lse^2).  red: LDS scratch of
+// W * (2*NP*EPL + 1) doubles, free once every wavefront reaches this call.
+template <int NP, int EPL, int W>
+__device__ __forceinline__ void block_stats(StatAcc<EPL>& sa, int lane, int wave,
+                                            double* red, double* __restrict__ row) {
+  constexpr int NPAD = NP * EPL;
+  constexpr int RS = 2 * NPAD + 1;
+#pragma unroll
+  for (int off = NP; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) {
+      sa.p[q] += __shfl_xor(sa.p[q], off, kWave);
+      sa.c[q] += __shfl_xor(sa.c[q], off, kWave);
+    }
+    sa.z2 += __shfl_xor(sa.z2, off, kWave);
+  }
+  __syncthreads();
+  if (lane < NP) {
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) {
+      red[wave * RS + lane + NP * q] = sa.p[q];
+      red[wave * RS + NPAD + lane + NP * q] = static_cast<double>(sa.c[q]);
+    }
+    if (lane == 0) red[wave * RS + 2 * NPAD] = sa.z2;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < RS; i += W * kWave) {
+    double v = 0.0;
+    for (int w = 0; w < W; ++w) v += red[w * RS + i];
+    row[i < NPAD ? i : i < 2 * NPAD ? kStatsCount + (i - NPAD) : kStatsZ] = v;
+  }
+}
+
+template <typename XT, int NP, int EPL, bool STATS>
 __global__ __launch_bounds__(kRouterThreads) void router_kernel(
     const XT* __restrict__ x, const float* __restrict__ wg, const float* __restrict__ bias,
     int T, int d, int Nr, int K, int gate, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w) {
+    float* __restrict__ topk_w, double* __restrict__ stats_part, float* __restrict__ lse) {
   constexpr int G = kWave / NP;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -112,7 +185,9 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(
   const int64_t tok0 =
       (static_cast<int64_t>(blockIdx.x) * (kRouterThreads / kWave) + wave) * (G * kTPL) +
       grp * kTPL;
-  if (tok0 >= T) return;
+  // With statistics every wavefront must reach the workgroup reduction; the
+  // clamped row pointers keep an idle group's loads in bounds.
+  if (!STATS && tok0 >= T) return;
 
   int e[EPL];
   bool ev[EPL];
@@ -160,24 +235,40 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(
 #pragma unroll
   for (int q = 0; q < EPL; ++q) bq[q] = (bias != nullptr && ev[q]) ? bias[e[q]] : 0.0f;
 
+  StatAcc<EPL> sa;
+  sa.zero();
   for (int i = 0; i < kTPL; ++i) {
     const int64_t t = tok0 + i;
     if (t >= T) break;  // uniform within the group
     float z[EPL];
 #pragma unroll
     for (int q = 0; q < EPL; ++q) z[q] = ev[q] ? acc[i][q] + bq[q] : -INFINITY;
-    select_and_store<NP, EPL>(z, e, ev, t, K, gate, grp, lane, topk_idx, topk_w);
+    select_and_store<NP, EPL, STATS>(z, e, ev, t, K, gate, grp, lane, topk_idx, topk_w, &sa, lse);
+  }
+  if constexpr (STATS) {
+    __shared__ double red[(kRouterThreads / kWave) * (2 * NP * EPL + 1)];
+    block_stats<NP, EPL, kRouterThreads / kWave>(sa, lane, wave, red,
+                                                 stats_part + static_cast<int64_t>(blockIdx.x) * kStatsStride);
   }
 }
 
+// Launches the vector-ALU router; returns the number of workgroups (the
+// rows of statistics written) through nblk.
 template <typename XT, int NP, int EPL>
-hipError_t launch_t(const RouteArgs& a, hipStream_t s) {
+hipError_t launch_t(const RouteArgs& a, hipStream_t s, int* nblk) {
   constexpr int G = kWave / NP;
   constexpr int tok_per_block = (kRouterThreads / kWave) * G * kTPL;
+  static_assert(tok_per_block >= 32, "route_stats_bytes assumes >= 32 tokens per workgroup");
   const int grid = (a.T + tok_per_block - 1) / tok_per_block;
-  hipLaunchKernelGGL((router_kernel<XT, NP, EPL>), dim3(grid), dim3(kRouterThreads), 0, s,
-                     static_cast<const XT*>(a.x), a.w_router, a.bias, a.T, a.d, a.n_routed,
-                     a.top_k, a.gate, a.topk_idx, a.topk_w);
+  *nblk = grid;
+  if (a.stats_part != nullptr)
+    hipLaunchKernelGGL((router_kernel<XT, NP, EPL, true>), dim3(grid), dim3(kRouterThreads), 0, s,
+                       static_cast<const XT*>(a.x), a.w_router, a.bias, a.T, a.d, a.n_routed,
+                       a.top_k, a.gate, a.topk_idx, a.topk_w, a.stats_part, a.lse);
+  else
+    hipLaunchKernelGGL((router_kernel<XT, NP, EPL, false>), dim3(grid), dim3(kRouterThreads), 0, s,
+                       static_cast<const XT*>(a.x), a.w_router, a.bias, a.T, a.d, a.n_routed,
+                       a.top_k, a.gate, a.topk_idx, a.topk_w, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -289,11 +380,12 @@ __device__ __forceinline__ void router_round(f32x16 (&acc)[MBLK][NBLK],
 // Small batches split K over KS workgroups per token block as well
 // (blockIdx.y); each then writes its summed tile to partial[ks][t][e] and
 // router_select_kernel finishes the sum in ks order and selects.
-template <int MBLK, int NBLK>
+template <int MBLK, int NBLK, bool STATS>
 __global__ __launch_bounds__(kRW * kWave) void router_mfma_kernel(
     const bf16_t* __restrict__ x, const float* __restrict__ wg, const float* __restrict__ bias,
     int T, int d, int Nr, int K, int gate, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w, int KS, float* __restrict__ partial) {
+    float* __restrict__ topk_w, int KS, float* __restrict__ partial,
+    double* __restrict__ stats_part, float* __restrict__ lse) {
   constexpr int TB = 32 * MBLK;
   constexpr int NPAD = 32 * NBLK;
   // Selection: groups of 16 lanes, one token each (4-step reductions).
@@ -303,7 +395,9 @@ __global__ __launch_bounds__(kRW * kWave) void router_mfma_kernel(
   constexpr int RS = 16 / MBLK;               // x slices per round
   constexpr int RD = (MBLK * NBLK <= 2) ? 4 : 2;  // W_g slices in flight
   static_assert((TB / kRW) % G == 0, "token split");
-  __shared__ float lg[TB][NPAD + 1];
+  __shared__ __align__(16) float lg[TB][NPAD + 1];
+  static_assert(!STATS || sizeof(lg) >= kRW * (2 * NPAD + 1) * sizeof(double),
+                "statistics reduction reuses the logit tile");
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -384,14 +478,19 @@ __global__ __launch_bounds__(kRW * kWave) void router_mfma_kernel(
     evq[q] = e[q] < Nr;
     bq[q] = (bias != nullptr && evq[q]) ? bias[e[q]] : 0.0f;
   }
+  StatAcc<EPL> sa;
+  sa.zero();
   for (int tl = wave * (TB / kRW) + grp; tl < (wave + 1) * (TB / kRW); tl += G) {
     const int64_t t = tok0 + tl;
     if (t >= T) break;  // uniform within the group
     float z[EPL];
 #pragma unroll
     for (int q = 0; q < EPL; ++q) z[q] = evq[q] ? lg[tl][e[q]] + bq[q] : -INFINITY;
-    select_and_store<NP, EPL>(z, e, evq, t, K, gate, grp, lane, topk_idx, topk_w);
+    select_and_store<NP, EPL, STATS>(z, e, evq, t, K, gate, grp, lane, topk_idx, topk_w, &sa, lse);
   }
+  if constexpr (STATS)
+    block_stats<NP, EPL, kRW>(sa, lane, wave, reinterpret_cast<double*>(&lg[0][0]),
+                              stats_part + static_cast<int64_t>(blockIdx.x) * kStatsStride);
 }
 
 // Logit (t, e) as the sum of the KS <= kRouterSplit partial tiles, in ks
@@ -438,14 +537,22 @@ __global__ __launch_bounds__(kWave) void router_select_kernel(
 }
 
 template <int MBLK, int NBLK>
-hipError_t launch_mfma(const RouteArgs& a, hipStream_t s) {
+hipError_t launch_mfma(const RouteArgs& a, hipStream_t s, int* nblk) {
   constexpr int TB = 32 * MBLK;
   const int blocks = (a.T + TB - 1) / TB;
+  *nblk = blocks;
+  if (a.stats_part != nullptr) {
+    hipLaunchKernelGGL((router_mfma_kernel<MBLK, NBLK, true>), dim3(blocks, 1), dim3(kRW * kWave), 0,
+                       s, static_cast<const bf16_t*>(a.x), a.w_router, a.bias, a.T, a.d,
+                       a.n_routed, a.top_k, a.gate, a.topk_idx, a.topk_w, 1, nullptr,
+                       a.stats_part, a.lse);
+    return hipGetLastError();
+  }
   // Split K when the token blocks alone would leave most CUs idle.
   const int KS = (a.partial != nullptr && MBLK == 1) ? max(1, min(kRouterSplit, 128 / blocks)) : 1;
-  hipLaunchKernelGGL((router_mfma_kernel<MBLK, NBLK>), dim3(blocks, KS), dim3(kRW * kWave), 0, s,
+  hipLaunchKernelGGL((router_mfma_kernel<MBLK, NBLK, false>), dim3(blocks, KS), dim3(kRW * kWave), 0, s,
                      static_cast<const bf16_t*>(a.x), a.w_router, a.bias, a.T, a.d, a.n_routed,
-                     a.top_k, a.gate, a.topk_idx, a.topk_w, KS, a.partial);
+                     a.top_k, a.gate, a.topk_idx, a.topk_w, KS, a.partial, nullptr, nullptr);
   if (KS == 1) return hipGetLastError();
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -455,29 +562,132 @@ hipError_t launch_mfma(const RouteArgs& a, hipStream_t s) {
 }
 
 template <typename XT>
-hipError_t launch_x(const RouteArgs& a, hipStream_t s) {
+hipError_t launch_x(const RouteArgs& a, hipStream_t s, int* nblk) {
   const int n = a.n_routed;
-  if (n <= 8) return launch_t<XT, 8, 1>(a, s);
-  if (n <= 16) return launch_t<XT, 16, 1>(a, s);
-  if (n <= 32) return launch_t<XT, 32, 1>(a, s);
-  if (n <= 64) return launch_t<XT, 64, 1>(a, s);
-  if (n <= 128) return launch_t<XT, 64, 2>(a, s);
-  return launch_t<XT, 64, 4>(a, s);
+  if (n <= 8) return launch_t<XT, 8, 1>(a, s, nblk);
+  if (n <= 16) return launch_t<XT, 16, 1>(a, s, nblk);
+  if (n <= 32) return launch_t<XT, 32, 1>(a, s, nblk);
+  if (n <= 64) return launch_t<XT, 64, 1>(a, s, nblk);
+  if (n <= 128) return launch_t<XT, 64, 2>(a, s, nblk);
+  return launch_t<XT, 64, 4>(a, s, nblk);
+}
+
+hipError_t launch_router(const RouteArgs& a, hipStream_t s, int* nblk) {
+  if (a.x_bf16 && a.d % 64 == 0) {
+    // Two token blocks per wavefront once there are enough tokens to fill
+    // the chip with 64-token workgroups.
+    const bool wide = a.T >= 64 * 256;
+    if (a.n_routed <= 32) return wide ? launch_mfma<2, 1>(a, s, nblk) : launch_mfma<1, 1>(a, s, nblk);
+    if (a.n_routed <= 64) return wide ? launch_mfma<2, 2>(a, s, nblk) : launch_mfma<1, 2>(a, s, nblk);
+    if (a.n_routed <= 128) return launch_mfma<1, 4>(a, s, nblk);
+  }
+  return a.x_bf16 ? launch_x<bf16_t>(a, s, nblk) : launch_x<float>(a, s, nblk);
+}
+
+constexpr int kFoldThreads = 1024;
+
+// Routing statistics from the router's per-workgroup rows (DeepSeekMoE page,
+// section 3.3, eq. 12-17; MoE-survey blog page, section 5, z-loss), one
+// workgroup.  Column sums run over the rows in a fixed order: wavefront w
+// takes rows w, w + 16, ... for 64 columns at a time, then the 16 partial
+// sums are added in wavefront order.  Then
+//   P_i = sum_s / T, f_i = count_i * N_r / (K' T),
+//   f'_g = mean of f over [g N_r/D, (g+1) N_r/D), P'_g = sum of P there,
+//   L_ExpBal = sum f_i P_i, L_DevBal = sum f'_g P'_g, z = sum lse^2 / T,
+// all in fp64, stored as fp32.  An empty batch gives zeros.
+__global__ __launch_bounds__(kFoldThreads) void route_stats_kernel(
+    const double* __restrict__ rows, int nblk, int T, int Nr, int K, int D,
+    float* __restrict__ stats) {
+  constexpr int W = kFoldThreads / kWave;
+  __shared__ double tot[kStatsStride];
+  __shared__ double red[W][kWave];
+  __shared__ double fv[256], pv[256], fd[256], pd[256];
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int ncol = 2 * Nr + 1;
+  for (int c0 = 0; c0 < ncol; c0 += kWave) {
+    const int ci = c0 + lane;
+    const int col = ci < Nr ? ci : ci < 2 * Nr ? kStatsCount + (ci - Nr) : kStatsZ;
+    double v = 0.0;
+    if (ci < ncol) {
+      int b = wave;
+      for (; b + 3 * W < nblk; b += 4 * W) {
+        const double r0 = rows[static_cast<int64_t>(b) * kStatsStride + col];
+        const double r1 = rows[static_cast<int64_t>(b + W) * kStatsStride + col];
+        const double r2 = rows[static_cast<int64_t>(b + 2 * W) * kStatsStride + col];
+        const double r3 = rows[static_cast<int64_t>(b + 3 * W) * kStatsStride + col];
+        v += r0;
+        v += r1;
+        v += r2;
+        v += r3;
+      }
+      for (; b < nblk; b += W) v += rows[static_cast<int64_t>(b) * kStatsStride + col];
+    }
+    red[wave][lane] = v;
+    __syncthreads();
+    if (wave == 0 && ci < ncol) {
+      double sum = 0.0;
+      for (int w = 0; w < W; ++w) sum += red[w][lane];
+      tot[col] = sum;
+    }
+    __syncthreads();
+  }
+  const double invT = T > 0 ? 1.0 / T : 0.0;
+  const double fscale = T > 0 ? static_cast<double>(Nr) / (static_cast<double>(K) * T) : 0.0;
+  for (int i = threadIdx.x; i < Nr; i += kFoldThreads) {
+    pv[i] = tot[i] * invT;
+    fv[i] = tot[kStatsCount + i] * fscale;
+    stats[i] = static_cast<float>(pv[i]);
+    stats[Nr + i] = static_cast<float>(fv[i]);
+  }
+  __syncthreads();
+  const int gs = Nr / D;
+  for (int g = threadIdx.x; g < D; g += kFoldThreads) {
+    double fs = 0.0, ps = 0.0;
+    for (int j = g * gs; j < (g + 1) * gs; ++j) {
+      fs += fv[j];
+      ps += pv[j];
+    }
+    fd[g] = fs / gs;
+    pd[g] = ps;
+    stats[2 * Nr + g] = static_cast<float>(fd[g]);
+    stats[2 * Nr + D + g] = static_cast<float>(pd[g]);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    double le = 0.0, ld = 0.0;
+    for (int i = lane; i < Nr; i += kWave) le += fv[i] * pv[i];
+    for (int g = lane; g < D; g += kWave) ld += fd[g] * pd[g];
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+      le += __shfl_xor(le, o, kWave);
+      ld += __shfl_xor(ld, o, kWave);
+    }
+    if (lane == 0) {
+      stats[2 * Nr + 2 * D] = static_cast<float>(le);
+      stats[2 * Nr + 2 * D + 1] = static_cast<float>(ld);
+      stats[2 * Nr + 2 * D + 2] = static_cast<float>(tot[kStatsZ] * invT);
+    }
+  }
 }
 
 }  // namespace
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  if (a.x_bf16 && a.d % 64 == 0) {
-    // Two token blocks per wavefront once there are enough tokens to fill
-    // the chip with 64-token workgroups.
-    const bool wide = a.T >= 64 * 256;
-    if (a.n_routed <= 32) return wide ? launch_mfma<2, 1>(a, s) : launch_mfma<1, 1>(a, s);
-    if (a.n_routed <= 64) return wide ? launch_mfma<2, 2>(a, s) : launch_mfma<1, 2>(a, s);
-    if (a.n_routed <= 128) return launch_mfma<1, 4>(a, s);
+  int nblk = 0;
+  return launch_router(a, s, &nblk);
+}
+
+hipError_t launch_route_stats(const RouteArgs& a, int n_devices, float* stats, hipStream_t s) {
+  int nblk = 0;
+  if (a.T > 0) {
+    const hipError_t err = launch_router(a, s, &nblk);
+    if (err != hipSuccess) return err;
   }
-  return a.x_bf16 ? launch_x<bf16_t>(a, s) : launch_x<float>(a, s);
+  hipLaunchKernelGGL(route_stats_kernel, dim3(1), dim3(kFoldThreads), 0, s,
+                     static_cast<const double*>(a.stats_part), nblk, a.T, a.n_routed, a.top_k,
+                     n_devices, stats);
+  return hipGetLastError();
 }
 
 }  // namespace moe

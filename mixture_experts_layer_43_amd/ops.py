@@ -93,6 +93,36 @@ def route(layer: Layer, x, w_router, bias=None):
     return idx, w
 
 
+def stats_len(layer: Layer, n_devices: int) -> int:
+    return 2 * layer.n_routed + 2 * n_devices + 3
+
+
+def split_stats(layer: Layer, n_devices: int, stats) -> dict:
+    """Name the parts of a moe_route_stats output vector (include/moe.h)."""
+    n, D = layer.n_routed, n_devices
+    return {"P": stats[:n], "f": stats[n:2 * n], "f_dev": stats[2 * n:2 * n + D],
+            "P_dev": stats[2 * n + D:2 * n + 2 * D], "l_exp": stats[2 * n + 2 * D],
+            "l_dev": stats[2 * n + 2 * D + 1], "z_loss": stats[2 * n + 2 * D + 2]}
+
+
+def route_stats(layer: Layer, x, w_router, bias=None, n_devices: int = 1, lse: bool = False,
+                ws=None):
+    """Router plus routing statistics: (topk_idx, topk_w, stats [2N+2D+3], lse [T] or None)."""
+    T = x.shape[0]
+    dt = layer.torch_dtype
+    _check(x, (T, layer.d_model), dt, "x")
+    _check(w_router, (layer.n_routed, layer.d_model), torch.float32, "w_router", x.device)
+    _check(bias, (layer.n_routed,), torch.float32, "bias", x.device)
+    idx = torch.empty((T, layer.top_k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, layer.top_k), dtype=torch.float32, device=x.device)
+    stats = torch.empty(stats_len(layer, n_devices), dtype=torch.float32, device=x.device)
+    l = torch.empty(T, dtype=torch.float32, device=x.device) if lse else None
+    ws = workspace(layer, T, x.device) if ws is None else ws
+    call("moe_route_stats", ctypes.byref(layer.c()), T, _p(x), _p(w_router), _p(bias), n_devices,
+         _p(idx), _p(w), _p(stats), _p(l), _p(ws), ws.numel(), _stream())
+    return idx, w, stats, l
+
+
 def permute(layer: Layer, topk_idx, x=None, ws=None):
     """Dispatch.  x given: also returns x_perm (rows of x in dispatch order)."""
     T = topk_idx.shape[0]

@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     L = _lib.lib()
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib.EXPORTS)
@@ -98,6 +98,25 @@ def test_route_argument_errors():
     assert L.moe_route(None, 16, *args, None) == MOE_ERR_INVALID_ARG
     # T == 0 is a valid no-op and must not touch the GPU
     assert L.moe_route(ctypes.byref(lay), 0, P(FAKE), P(FAKE), None, P(FAKE), P(FAKE), None) == MOE_OK
+
+
+def test_route_stats_argument_errors():
+    L = _lib.lib()
+    lay = layer()
+    P = ctypes.c_void_p
+    f = P(FAKE)
+    st, need = ws_size(lay, 64)
+
+    def call(D=8, stats=f, lse=None, ws_bytes=need):
+        return L.moe_route_stats(ctypes.byref(lay), 64, f, f, None, D, f, f, stats, lse, f,
+                                 ws_bytes, None)
+
+    assert call(D=0) == MOE_ERR_INVALID_ARG
+    assert call(D=5) == MOE_ERR_INVALID_ARG          # 5 does not divide N_r = 64
+    assert call(D=-2) == MOE_ERR_INVALID_ARG
+    assert call(stats=None) == MOE_ERR_INVALID_ARG
+    assert call(lse=P(UNALIGNED)) == MOE_ERR_UNSUPPORTED
+    assert call(ws_bytes=need - 1) == MOE_ERR_WORKSPACE_TOO_SMALL
 
 
 def test_workspace_too_small_is_rejected_before_launch():

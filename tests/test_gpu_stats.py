@@ -1,0 +1,145 @@
+"""GPU parity of moe_route_stats (routing statistics) against the oracle.
+
+DeepSeekMoE page, section 3.3, eq. 12-17 (expert- and device-level balance)
+and the MoE-survey blog page, sections 4-5 (Switch balance loss, router
+z-loss).  Every call goes through the C ABI.
+
+Tolerances (from the arithmetic):
+  topk_idx bit-exact against the oracle, and topk_idx / topk_w bit-identical
+  to moe_route's (the same kernel sums the logits in the same order);
+  f_i, f'_g: the choice counts are exact integers and both sides form
+    count * N/(K'T) in fp64, so only the final fp32 rounding differs:
+    relative 2e-7;
+  P_i, P'_g, L_ExpBal, L_DevBal: every s_{i,t} is within the gate tolerance
+    (2e-5 relative) of the oracle's, sums of non-negative terms keep that
+    relative bound, and f is exact: relative 2e-5 (absolute 1e-30 for
+    probabilities that underflow);
+  lse_t: the logits' fp32 error shifts it by at most about the same amount
+    as the gates: |d| <= 2e-5 * (1 + |lse|); z-loss, the mean of lse^2,
+    doubles that relative bound: |d| <= 4e-5 * (1 + z).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _parity import host, prepare, upload
+from mixture_experts_layer_43_amd import ops
+from synth import LayerConfig, get_config
+from test_gpu_parity import MID, announce, cfg_of
+
+pytestmark = pytest.mark.gpu
+
+
+def stats_ref(cfg, inp, D):
+    x = oracle.decode(inp["x"], cfg.dtype)
+    b = None if inp.get("bias") is None else np.asarray(inp["bias"], np.float64)
+    z = oracle.router_logits(x, np.asarray(inp["w_router"], np.float64), b)
+    idx, g = oracle.route(z, cfg.top_k, cfg.gate)
+    return idx, g, oracle.routing_stats(z, idx, D)
+
+
+def check_stats(lay, D, stats, lse, ref):
+    got = ops.split_stats(lay, D, host(stats).astype(np.float64))
+    for k in ("f", "f_dev"):
+        np.testing.assert_allclose(got[k], ref[k], rtol=2e-7, atol=0, err_msg=k)
+    for k in ("P", "P_dev"):
+        np.testing.assert_allclose(got[k], ref[k], rtol=2e-5, atol=1e-30, err_msg=k)
+    for k in ("l_exp", "l_dev"):
+        assert abs(got[k] - ref[k]) <= 2e-5 * ref[k], (k, got[k], ref[k])
+    assert abs(got["z_loss"] - ref["z_loss"]) <= 4e-5 * (1 + ref["z_loss"]), (got["z_loss"], ref["z_loss"])
+    if lse is not None:
+        d = np.abs(host(lse).astype(np.float64) - ref["lse"])
+        assert (d <= 2e-5 * (1 + np.abs(ref["lse"]))).all(), f"lse off by up to {d.max():.3e}"
+
+
+def run_case(cfg, inp, D, want_lse=True):
+    lay = ops.Layer.of(cfg)
+    d = upload(inp)
+    idx, w, stats, lse = ops.route_stats(lay, d["x"], d["w_router"], d["bias"], D, lse=want_lse)
+    torch.cuda.synchronize()
+    return lay, d, idx, w, stats, lse
+
+
+CASES = [("tiny-f32", 4), ("mid-ragged", 4), ("mid-ragged", 1), ("mid-ragged", 16),
+         ("mid-gshard", 2), ("mid-f32", 3), ("mid-wide-k", 10), ("mid-many-experts", 8),
+         ("mid-many-tokens", 6), ("16b-decode", 8), ("2b", 9), ("16b", 8), ("gshard-zipf", 8)]
+
+
+@pytest.mark.parametrize("name,D", CASES, ids=[f"{n}-D{D}" for n, D in CASES])
+def test_route_stats_matches_oracle(name, D):
+    cfg = cfg_of(name)
+    announce(f"route_stats {name} T={cfg.tokens} D={D}")
+    inp = prepare(cfg)
+    ref_idx, ref_w, ref = stats_ref(cfg, inp, D)
+    lay, d, idx, w, stats, lse = run_case(cfg, inp, D)
+    np.testing.assert_array_equal(host(idx), ref_idx)
+    # Same routing as moe_route, bit for bit.
+    idx0, w0 = ops.route(lay, d["x"], d["w_router"], d["bias"])
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx0) and torch.equal(w, w0)
+    check_stats(lay, D, stats, lse, ref)
+
+
+@pytest.mark.parametrize("T", [1, 31, 33, 65, 257])
+@pytest.mark.parametrize("base", ["mid-ragged", "mid-f32"])
+def test_route_stats_ragged_batches(base, T):
+    cfg = MID[base].with_(tokens=T, seed=500 + T)
+    announce(f"route_stats {base} T={T}")
+    inp = prepare(cfg)
+    _, _, ref = stats_ref(cfg, inp, 2)
+    lay, _, _, _, stats, lse = run_case(cfg, inp, 2)
+    check_stats(lay, 2, stats, lse, ref)
+
+
+def test_route_stats_top1_is_switch_loss():
+    """K' = 1: L_ExpBal is the Switch balance loss N sum_i f_i P_i with f_i the
+    arg-max share (MoE-survey blog page, section 4), computed on the host from
+    the oracle's logits by arg-max and bincount."""
+    cfg = MID["mid-gshard"].with_(top_k=1, gate="softmax_topk", seed=610)
+    announce("route_stats top-1")
+    inp = prepare(cfg)
+    x = oracle.decode(inp["x"], cfg.dtype)
+    z = oracle.router_logits(x, np.asarray(inp["w_router"], np.float64),
+                             np.asarray(inp["bias"], np.float64))
+    p = np.exp(z - z.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    share = np.bincount(p.argmax(1), minlength=cfg.n_routed) / cfg.tokens
+    switch = cfg.n_routed * float(share @ p.mean(0))
+    lay, _, _, _, stats, _ = run_case(cfg, inp, 1, want_lse=False)
+    got = ops.split_stats(lay, 1, host(stats).astype(np.float64))
+    assert abs(got["l_exp"] - switch) <= 2e-5 * switch
+
+
+def test_route_stats_forced_experts():
+    """A large bias sends every token to experts 5 and 11: f is N/K' there and
+    0 elsewhere, and nearly all probability sits on the two."""
+    cfg = MID["mid-ragged"].with_(tokens=500, top_k=2, seed=620)
+    inp = prepare(cfg)
+    bias = np.zeros(cfg.n_routed, np.float32)
+    bias[[5, 11]] = 40.0
+    inp["bias"] = bias
+    announce("route_stats forced experts")
+    _, _, ref = stats_ref(cfg, inp, 4)
+    lay, _, _, _, stats, lse = run_case(cfg, inp, 4)
+    check_stats(lay, 4, stats, lse, ref)
+    got = ops.split_stats(lay, 4, host(stats))
+    f = np.zeros(cfg.n_routed)
+    f[[5, 11]] = cfg.n_routed / 2
+    np.testing.assert_array_equal(got["f"], f)
+
+
+def test_route_stats_deterministic_and_empty():
+    cfg, D = MID["mid-many-tokens"], 3
+    announce("route_stats determinism, empty batch")
+    inp = prepare(cfg)
+    lay, d, _, _, a, la = run_case(cfg, inp, D)
+    _, _, b, lb = ops.route_stats(lay, d["x"], d["w_router"], d["bias"], D, lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(la, lb)
+    x0 = torch.zeros((0, cfg.d_model), dtype=lay.torch_dtype, device="cuda")
+    _, _, s0, _ = ops.route_stats(lay, x0, d["w_router"], d["bias"], D)
+    torch.cuda.synchronize()
+    assert (host(s0) == 0).all() and s0.numel() == 2 * cfg.n_routed + 2 * D + 3
