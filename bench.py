@@ -186,6 +186,36 @@ def main():
         hip.hipEventDestroy(ev)
     st = dict(zip(_lib.STAGES, stage_ms.mean(0).round(5).tolist()))
 
+    # Routing statistics (moe_route_stats) next to the plain router on the
+    # same batch, outside the timed region: the cost of the statistics.
+    def per_call_ms(fn, n=20):
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    n_dev = 8 if cfg.n_routed % 8 == 0 else 1
+    s_idx, s_w, s_stats, s_lse = ops.route_stats(lay, d["x"], d["w_router"], d["bias"], n_dev, lse=True,
+                                                 ws=fwd.ws)
+
+    def route_plain():
+        _lib.check("moe_route", lib.moe_route(ctypes.byref(c_layer), cfg.tokens, p(d["x"]),
+                                              p(d["w_router"]), p(d["bias"]), p(s_idx), p(s_w), stream))
+
+    def route_with_stats():
+        _lib.check("moe_route_stats", lib.moe_route_stats(
+            ctypes.byref(c_layer), cfg.tokens, p(d["x"]), p(d["w_router"]), p(d["bias"]), n_dev,
+            p(s_idx), p(s_w), p(s_stats), p(s_lse), p(fwd.ws), fwd.ws.numel(), stream))
+
+    route_ms = per_call_ms(route_plain)
+    route_stats_ms = per_call_ms(route_with_stats)
+
     T, dm, I, K = cfg.tokens, cfg.d_model, cfg.d_ff, cfg.top_k
     P = T * K
     # With I_s == I the shared experts run as K_s extra groups of T rows in
@@ -250,6 +280,8 @@ def main():
         "expert_gemm_frac_mfma": expert_tflops / PEAK_BF16_TFLOPS,
         "layer_tflops": layer_tflops,
         "stage_ms": st,
+        "routing_stats": {"route_ms": route_ms, "route_stats_ms": route_stats_ms,
+                          "n_devices": n_dev},
         "layer_algorithmic_bytes": layer_bytes,
         "layer_hbm_gbs": layer_gbs,
         "layer_hbm_frac": layer_gbs / PEAK_HBM_GBS,

@@ -46,7 +46,6 @@ Layout layout_of(const moe_layer* L, int64_t T) {
     return at;
   };
   o.router_part = take(moe::router_partial_bytes(T));
-  o.stats_part = take(moe::route_stats_bytes(T));
   o.block_counts = take(NB * Nr * 4);
   o.block_base = take(NB * Nr * 4);
   o.local_rank = take(P * 4);
@@ -64,6 +63,7 @@ Layout layout_of(const moe_layer* L, int64_t T) {
   o.h_shared = o.h;
   o.y_perm = take(R * d * e);
   o.y_shared = take(L->n_shared > 0 && !fold_shared(L) ? static_cast<size_t>(T) * d * e : 0);
+  o.stats_part = take(moe::route_stats_bytes(T));   // moe_route_stats only
   o.total = cur;
   return o;
 }

@@ -588,13 +588,15 @@ constexpr int kFoldThreads = 1024;
 
 // Routing statistics from the router's per-workgroup rows (DeepSeekMoE page,
 // section 3.3, eq. 12-17; MoE-survey blog page, section 5, z-loss), one
-// workgroup.  Column sums run over the rows in a fixed order: wavefront w
-// takes rows w, w + 16, ... for 64 columns at a time, then the 16 partial
-// sums are added in wavefront order.  Then
+// workgroup.  The 2 N_r + 1 used columns are taken in NCH chunks of 64, one
+// per lane; wavefront w sums rows w, w + 16, ... (every chunk's load for a
+// row issued together, no branches), then the 16 partial sums are added in
+// wavefront order, so the result does not depend on timing.  Then
 //   P_i = sum_s / T, f_i = count_i * N_r / (K' T),
 //   f'_g = mean of f over [g N_r/D, (g+1) N_r/D), P'_g = sum of P there,
 //   L_ExpBal = sum f_i P_i, L_DevBal = sum f'_g P'_g, z = sum lse^2 / T,
 // all in fp64, stored as fp32.  An empty batch gives zeros.
+template <int NCH>
 __global__ __launch_bounds__(kFoldThreads) void route_stats_kernel(
     const double* __restrict__ rows, int nblk, int T, int Nr, int K, int D,
     float* __restrict__ stats) {
@@ -604,30 +606,33 @@ __global__ __launch_bounds__(kFoldThreads) void route_stats_kernel(
   __shared__ double fv[256], pv[256], fd[256], pd[256];
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int ncol = 2 * Nr + 1;
-  for (int c0 = 0; c0 < ncol; c0 += kWave) {
-    const int ci = c0 + lane;
-    const int col = ci < Nr ? ci : ci < 2 * Nr ? kStatsCount + (ci - Nr) : kStatsZ;
-    double v = 0.0;
-    if (ci < ncol) {
-      int b = wave;
-      for (; b + 3 * W < nblk; b += 4 * W) {
-        const double r0 = rows[static_cast<int64_t>(b) * kStatsStride + col];
-        const double r1 = rows[static_cast<int64_t>(b + W) * kStatsStride + col];
-        const double r2 = rows[static_cast<int64_t>(b + 2 * W) * kStatsStride + col];
-        const double r3 = rows[static_cast<int64_t>(b + 3 * W) * kStatsStride + col];
-        v += r0;
-        v += r1;
-        v += r2;
-        v += r3;
-      }
-      for (; b < nblk; b += W) v += rows[static_cast<int64_t>(b) * kStatsStride + col];
-    }
-    red[wave][lane] = v;
+  int col[NCH];
+  bool used[NCH];
+  double v[NCH];
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) {
+    const int ci = ch * kWave + lane;
+    used[ch] = ci < ncol;
+    col[ch] = ci < Nr ? ci : ci < 2 * Nr ? kStatsCount + (ci - Nr) : kStatsZ;
+    v[ch] = 0.0;
+  }
+#pragma unroll 2
+  for (int b = wave; b < nblk; b += W) {
+    const double* r = rows + static_cast<int64_t>(b) * kStatsStride;
+    double x[NCH];
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) x[ch] = r[col[ch]];
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) v[ch] += used[ch] ? x[ch] : 0.0;
+  }
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) {
+    red[wave][lane] = v[ch];
     __syncthreads();
-    if (wave == 0 && ci < ncol) {
+    if (wave == 0 && used[ch]) {
       double sum = 0.0;
       for (int w = 0; w < W; ++w) sum += red[w][lane];
-      tot[col] = sum;
+      tot[col[ch]] = sum;
     }
     __syncthreads();
   }
@@ -684,9 +689,19 @@ hipError_t launch_route_stats(const RouteArgs& a, int n_devices, float* stats, h
     const hipError_t err = launch_router(a, s, &nblk);
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(route_stats_kernel, dim3(1), dim3(kFoldThreads), 0, s,
-                     static_cast<const double*>(a.stats_part), nblk, a.T, a.n_routed, a.top_k,
-                     n_devices, stats);
+  const int nch = (2 * a.n_routed + 1 + kWave - 1) / kWave;
+  const double* rows = a.stats_part;
+#define MOE_FOLD(N)                                                                              \
+  case N:                                                                                        \
+    hipLaunchKernelGGL(route_stats_kernel<N>, dim3(1), dim3(kFoldThreads), 0, s, rows, nblk, a.T, \
+                       a.n_routed, a.top_k, n_devices, stats);                                   \
+    break;
+  switch (nch) {
+    MOE_FOLD(1) MOE_FOLD(2) MOE_FOLD(3) MOE_FOLD(4) MOE_FOLD(5) MOE_FOLD(6) MOE_FOLD(7)
+    MOE_FOLD(8) MOE_FOLD(9)
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_FOLD
   return hipGetLastError();
 }
 
