@@ -6,7 +6,8 @@ The HIP library never calls into it and it never calls into the HIP library;
 the two share nothing except the seeded inputs from `synth`.
 
 Every function is pinned by tests/test_oracle_pins.py (the layer) and
-tests/test_oracle_stats_pins.py (routing statistics) against closed forms,
+tests/test_oracle_stats_pins.py (routing statistics) and
+tests/test_oracle_capacity_pins.py (capacity-limited dispatch) against closed forms,
 special cases and a pure-Python brute force (see tests/_brute.py).
 """
 from .moe import (  # noqa: F401
@@ -24,3 +25,4 @@ from .moe import (  # noqa: F401
 )
 from .gap import enforce_gap, topk_gap  # noqa: F401
 from .stats import routing_stats  # noqa: F401
+from .capacity import capacity_for, dispatch_capacity, keep_mask  # noqa: F401

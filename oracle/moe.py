@@ -24,10 +24,15 @@ Readings taken where the pages leave a step open:
     in ascending order.
   * shared experts enter with weight 1 (eq. 9, first sum); the residual
     u_t of eq. 9 is added only when asked for.
+  * with cfg.capacity > 0 the dispatch keeps at most that many assignments
+    per expert and token group ([P4] section 3, expert capacity; readings in
+    oracle/capacity.py) and a dropped assignment contributes nothing.
 """
 from __future__ import annotations
 
 import numpy as np
+
+from .capacity import dispatch_capacity
 
 GATES = ("softmax_topk", "topk_softmax")
 
@@ -141,7 +146,13 @@ def forward(cfg, inputs: dict, tokens=None, residual: bool = False) -> dict:
 
     z = router_logits(x, wr, b)
     idx, g = route(z, k, cfg.gate)
-    counts, offsets, row_token, slot_row = dispatch(idx, Nr)
+    cap = getattr(cfg, "capacity", 0)
+    if cap > 0:
+        # Expert capacity ([P4] section 3): dropped assignments get gate 0.
+        counts, offsets, row_token, slot_row, kept = dispatch_capacity(idx, Nr, cap, cfg.group_size)
+    else:
+        counts, offsets, row_token, slot_row = dispatch(idx, Nr)
+        kept = np.ones(idx.shape, dtype=bool)
 
     sel = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
     pos = np.full(T, -1, dtype=np.int64)
@@ -152,11 +163,11 @@ def forward(cfg, inputs: dict, tokens=None, residual: bool = False) -> dict:
     for e in range(Nr):
         rows = np.arange(offsets[e], offsets[e + 1])
         toks = row_token[rows]
-        keep = pos[toks] >= 0
-        if not np.any(keep):
+        want = pos[toks] >= 0
+        if not np.any(want):
             continue
-        toks = toks[keep]
-        slots = np.nonzero(idx[toks] == e)[1]
+        toks = toks[want]
+        slots = np.nonzero(idx[toks] == e)[1]   # rows hold kept assignments only
         ge = g[toks, slots]
         F = expert_ffn(x[toks], decode(inputs["w_gate"][e], dt),
                        decode(inputs["w_up"][e], dt), decode(inputs["w_down"][e], dt))
@@ -170,5 +181,5 @@ def forward(cfg, inputs: dict, tokens=None, residual: bool = False) -> dict:
 
     return {
         "logits": z, "topk_idx": idx, "topk_w": g, "counts": counts, "offsets": offsets,
-        "row_token": row_token, "slot_row": slot_row, "tokens": sel, "y": y,
+        "row_token": row_token, "slot_row": slot_row, "tokens": sel, "y": y, "kept": kept,
     }

@@ -50,15 +50,29 @@ def _gates(z, k, gate):
 
 
 def brute_forward(x, w_router, bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
-                  top_k, gate, residual=False):
+                  top_k, gate, residual=False, capacity=0, group_size=0):
     """All arguments are nested Python lists of floats (bias may be None).
+
+    capacity > 0: each expert takes at most `capacity` tokens per group of
+    `group_size` consecutive tokens (0: the whole batch), first come first
+    served in token order; a token that finds a chosen expert full loses that
+    expert's gate (MoE-survey blog page, section 3, expert capacity).
 
     Returns (chosen ids per token, ascending; dense gates per token; y)."""
     chosen_all, g_all, y_all = [], [], []
     n = len(w_router)
-    for u in x:
+    S = group_size if 0 < group_size < len(x) else len(x)
+    taken = {}
+    for t, u in enumerate(x):
         z = [_dot(w_router[i], u) + (bias[i] if bias is not None else 0.0) for i in range(n)]
         chosen, g = _gates(z, top_k, gate)
+        if capacity > 0:
+            for i in chosen:
+                key = (t // S, i)
+                if taken.get(key, 0) < capacity:
+                    taken[key] = taken.get(key, 0) + 1
+                else:
+                    g[i] = 0.0
         y = [0.0] * len(u)
         for i in range(n):                       # dense: every routed expert
             f = _ffn(u, w_gate[i], w_up[i], w_down[i])
