@@ -52,11 +52,12 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
   MOE_OK = 0,
-  MOE_ERR_INVALID_ARG = 1,          /* null required pointer, T < 0, bad enum, K' out of range */
+  MOE_ERR_INVALID_ARG = 1,          /* null required pointer, T < 0, bad enum, K' out of range,
+                                       negative capacity or group_size                          */
   MOE_ERR_UNSUPPORTED = 2,          /* shape/alignment outside the supported set above         */
   MOE_ERR_WORKSPACE_TOO_SMALL = 3,  /* ws_bytes below moe_workspace_size()                      */
   MOE_ERR_HIP = 4                   /* a HIP launch or query failed                              */
@@ -73,7 +74,18 @@ typedef enum {
   MOE_GATE_TOPK_SOFTMAX = 1
 } moe_gate;
 
-/* Shape of one layer.  n_routed = N_r = mN - K_s, top_k = K' = mK - K_s. */
+/* Shape of one layer.  n_routed = N_r = mN - K_s, top_k = K' = mK - K_s.
+ *
+ * Expert capacity (MoE-survey blog page, section 3, GShard: expert capacity
+ * with a running counter per expert and local group dispatching; section 4,
+ * Switch: capacity = tokens / experts x capacity factor).  With capacity
+ * C > 0 the tokens are cut into groups of S = group_size consecutive tokens
+ * (the last group may be shorter; group_size 0, or >= T, is one group), and
+ * in every group each expert keeps its first C assignments in token order.
+ * A dropped assignment has gate zero: moe_permute gives it slot_row -1 and no
+ * row, the expert FFN never sees it and moe_combine adds nothing for it, so a
+ * token with all K' assignments dropped gets only the shared experts and the
+ * residual.  topk_w keeps the router's gate values.  capacity 0 = dropless. */
 typedef struct {
   int32_t d_model;      /* d                                  */
   int32_t n_routed;     /* N_r                                */
@@ -83,6 +95,8 @@ typedef struct {
   int32_t d_ff_shared;  /* I_s, width of one shared expert    */
   int32_t gate;         /* moe_gate                           */
   int32_t dtype;        /* moe_dtype                          */
+  int32_t capacity;     /* C, slots per expert per group; 0 = no limit */
+  int32_t group_size;   /* S, tokens per capacity group; 0 = all T     */
 } moe_layer;
 
 int moe_abi_version(void);
@@ -137,7 +151,11 @@ int moe_route_stats(const moe_layer* layer, int64_t T, const void* x, const floa
  *   input is undefined behaviour), x [T, d] (dtype)
  *   -> counts [N_r], offsets [N_r + 1] (exclusive scan, offsets[N_r] = P),
  *      row_token [P] (token of each row), slot_row [P] (row of slot t*K'+j),
- *      x_perm [P, d] (x_perm[r] = x[row_token[r]]; NULL skips the copy). */
+ *      x_perm [P, d] (x_perm[r] = x[row_token[r]]; NULL skips the copy).
+ * With layer->capacity > 0 only the kept assignments get rows: counts and
+ * offsets count kept rows (offsets[N_r] <= P), rows past offsets[N_r] of
+ * row_token and x_perm are left unwritten, and slot_row is -1 for a dropped
+ * slot. */
 int moe_permute(const moe_layer* layer, int64_t T, const int32_t* topk_idx, const void* x,
                 int32_t* counts, int32_t* offsets, int32_t* row_token, int32_t* slot_row,
                 void* x_perm, void* ws, size_t ws_bytes, void* stream);
@@ -160,8 +178,9 @@ int moe_shared_ffn(const moe_layer* layer, int64_t T, const void* x, const void*
 
 /* Gate-weighted combine (eq. 9):
  *   y[t] = sum_j topk_w[t,j] * y_perm[slot_row[t*K'+j]] + y_shared[t] + residual[t]
- * in fp32, j ascending, one rounding to dtype.  y_shared and residual may be
- * NULL (then omitted).  y [T, d]. */
+ * in fp32, j ascending, one rounding to dtype.  A slot with slot_row -1 (an
+ * assignment dropped by the expert capacity) adds nothing.  y_shared and
+ * residual may be NULL (then omitted).  y [T, d]. */
 int moe_combine(const moe_layer* layer, int64_t T, const void* y_perm, const int32_t* slot_row,
                 const float* topk_w, const void* y_shared, const void* residual, void* y,
                 void* stream);
@@ -174,7 +193,8 @@ int moe_combine(const moe_layer* layer, int64_t T, const void* y_perm, const int
  * dtype) instead of one y_shared row; otherwise they run as in
  * moe_shared_ffn.  residual (NULL or [T, d], usually x itself) is added
  * last.  topk_idx, topk_w, counts and offsets are written for inspection
- * and may be NULL (then they live in ws).  y [T, d]. */
+ * and may be NULL (then they live in ws).  The expert capacity of the
+ * layer applies as in moe_permute.  y [T, d]. */
 int moe_forward(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
                 const float* logit_bias, const void* w_gate, const void* w_up,
                 const void* w_down, const void* ws_gate, const void* ws_up,

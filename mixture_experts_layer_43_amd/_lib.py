@@ -23,7 +23,8 @@ STAGES = ("route", "dispatch", "routed_gate_up", "routed_down", "shared_gate_up"
 
 class MoeLayer(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
-        "d_model", "n_routed", "n_shared", "top_k", "d_ff", "d_ff_shared", "gate", "dtype")]
+        "d_model", "n_routed", "n_shared", "top_k", "d_ff", "d_ff_shared", "gate", "dtype",
+        "capacity", "group_size")]
 
 
 class MoeError(RuntimeError):

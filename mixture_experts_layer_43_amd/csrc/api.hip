@@ -17,6 +17,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
+  size_t cap_counts, cap_offsets, cap_row_token, cap_slot_row, cap_start, cap_base;
   size_t router_part, stats_part, block_counts, block_base, local_rank, topk_idx, topk_w, counts, offsets, row_token,
       slot_row, h, y_perm, h_shared, y_shared, total;
 };
@@ -31,6 +32,15 @@ bool fold_shared(const moe_layer* L) { return L->n_shared > 0 && L->d_ff_shared 
 // K_s blocks of T rows when the shared experts are folded in.
 int64_t forward_rows(const moe_layer* L, int64_t T) {
   return T * L->top_k + (fold_shared(L) ? T * L->n_shared : 0);
+}
+
+// Expert capacity: tokens per group (S) and number of groups (G).
+int64_t cap_group_len(const moe_layer* L, int64_t T) {
+  return (L->group_size > 0 && L->group_size < T) ? L->group_size : std::max<int64_t>(T, 1);
+}
+int64_t cap_groups(const moe_layer* L, int64_t T) {
+  const int64_t S = cap_group_len(L, T);
+  return std::max<int64_t>(1, (T + S - 1) / S);
 }
 
 Layout layout_of(const moe_layer* L, int64_t T) {
@@ -64,6 +74,15 @@ Layout layout_of(const moe_layer* L, int64_t T) {
   o.y_perm = take(R * d * e);
   o.y_shared = take(L->n_shared > 0 && !fold_shared(L) ? static_cast<size_t>(T) * d * e : 0);
   o.stats_part = take(moe::route_stats_bytes(T));   // moe_route_stats only
+  // Expert capacity: the dropless dispatch and the per-group tables.
+  const bool cap = L->capacity > 0;
+  const size_t G = static_cast<size_t>(cap_groups(L, T));
+  o.cap_counts = take(cap ? Nr * 4 : 0);
+  o.cap_offsets = take(cap ? (Nr + 1) * 4 : 0);
+  o.cap_row_token = take(cap ? P * 4 : 0);
+  o.cap_slot_row = take(cap ? P * 4 : 0);
+  o.cap_start = take(cap ? (G + 1) * Nr * 4 : 0);
+  o.cap_base = take(cap ? G * Nr * 4 : 0);
   o.total = cur;
   return o;
 }
@@ -77,6 +96,7 @@ int check_layer(const moe_layer* L, int64_t T) {
   if (L->d_model <= 0 || L->n_routed <= 0 || L->n_shared < 0 || L->d_ff <= 0)
     return MOE_ERR_INVALID_ARG;
   if (L->n_shared > 0 && L->d_ff_shared <= 0) return MOE_ERR_INVALID_ARG;
+  if (L->capacity < 0 || L->group_size < 0) return MOE_ERR_INVALID_ARG;
   if (L->top_k < 1 || L->top_k > L->n_routed || L->top_k > 16) return MOE_ERR_INVALID_ARG;
   if (L->n_routed > 256) return MOE_ERR_UNSUPPORTED;
   if (T >= (int64_t{1} << 31) / 16) return MOE_ERR_UNSUPPORTED;
@@ -364,6 +384,15 @@ static moe::PermuteArgs permute_args(const moe_layer* layer, int64_t T, const in
   a.block_counts = reinterpret_cast<int32_t*>(at(ws, lo.block_counts));
   a.block_base = reinterpret_cast<int32_t*>(at(ws, lo.block_base));
   a.local_rank = reinterpret_cast<int32_t*>(at(ws, lo.local_rank));
+  a.capacity = layer->capacity;
+  a.group_len = static_cast<int>(cap_group_len(layer, T));
+  a.n_groups = static_cast<int>(cap_groups(layer, T));
+  a.full_counts = reinterpret_cast<int32_t*>(at(ws, lo.cap_counts));
+  a.full_offsets = reinterpret_cast<int32_t*>(at(ws, lo.cap_offsets));
+  a.full_row_token = reinterpret_cast<int32_t*>(at(ws, lo.cap_row_token));
+  a.full_slot_row = reinterpret_cast<int32_t*>(at(ws, lo.cap_slot_row));
+  a.group_start = reinterpret_cast<int32_t*>(at(ws, lo.cap_start));
+  a.group_base = reinterpret_cast<int32_t*>(at(ws, lo.cap_base));
   return a;
 }
 

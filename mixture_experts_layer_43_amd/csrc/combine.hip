@@ -3,7 +3,8 @@
 // Each token's K' expert rows are gathered through slot_row and accumulated
 // in fp32 in ascending j, then the shared-expert rows (one sum, or one row
 // per shared expert in order) and the residual are added, and the sum is
-// rounded once.
+// rounded once.  A slot dropped by the expert capacity (slot_row -1) adds
+// nothing.
 // Pure streaming: bound by HBM bandwidth.
 #include "common.h"
 #include "kernels.h"
@@ -76,10 +77,15 @@ __global__ __launch_bounds__(256) void combine_kernel(
     // rows past the end re-read the last row, columns past the end re-read
     // the last chunk; neither is used.
     float v[JG][CPL][N];
+    bool dropped[JG];
 #pragma unroll
     for (int jj = 0; jj < JG; ++jj) {
       const int j = min(j0 + jj, nrows - 1);
-      const char* routed = y_perm + static_cast<int64_t>(slot_row[t * K + min(j, K - 1)]) * row_bytes;
+      // slot_row -1: an assignment dropped by the expert capacity (gate 0);
+      // row 0 is read in its place and not used.
+      const int sr = slot_row[t * K + min(j, K - 1)];
+      dropped[jj] = j < K && sr < 0;
+      const char* routed = y_perm + static_cast<int64_t>(max(sr, 0)) * row_bytes;
       const char* shared = (shared_blocks > 0 ? y_shared : y_perm) +
                            max(j - K, 0) * shared_stride_bytes + t * row_bytes;
       const char* res = (residual != nullptr ? residual : y_perm) + t * row_bytes;
@@ -94,6 +100,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
     for (int jj = 0; jj < JG; ++jj) {
       const int j = j0 + jj;
       if (j >= nrows) break;
+      if (dropped[jj]) continue;  // uniform: one token per wavefront
       const float w = j < K ? topk_w[t * K + j] : 1.0f;
 #pragma unroll
       for (int i = 0; i < CPL; ++i)

@@ -188,15 +188,130 @@ __global__ __launch_bounds__(kSmallTokens) void dispatch_small_kernel(
   small_dispatch(idx, T, K, Nr, counts, offsets, row_token, slot_row, sh);
 }
 
-}  // namespace
-
-hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
-  if (a.T == 0) {
-    // Empty batch: all counts and offsets are zero.
-    hipError_t err = launch_zero(a.counts, sizeof(int32_t) * a.n_routed, s);
-    if (err != hipSuccess) return err;
-    return launch_zero(a.offsets, sizeof(int32_t) * (a.n_routed + 1), s);
+// ---- expert capacity ---------------------------------------------------------
+// GShard's expert capacity with local group dispatching (MoE-survey blog page,
+// section 3; Switch, section 4): in every group of S consecutive tokens an
+// expert keeps its first C assignments in token order, the rest are dropped.
+// Built on the dropless dispatch, whose rows of expert e already hold its
+// tokens in ascending order:
+//   bounds   start[g][e] = number of e's rows whose token is below g*S (binary
+//            search in e's sorted rows), g = 0..G
+//   scan     kept(e, g) = min(start[g+1][e] - start[g][e], C); one exclusive
+//            scan in (e, g) order gives every (expert, group) its first row,
+//            and the counts and offsets of the kept rows
+//   scatter  the slot of token t with dropless row r of expert e has rank
+//            q = r - full_offsets[e] - start[t/S][e] inside its group; it
+//            keeps row base[e][t/S] + q when q < C, else slot_row = -1.
+__global__ __launch_bounds__(256) void cap_bounds_kernel(
+    const int32_t* __restrict__ full_row_token, const int32_t* __restrict__ full_offsets, int S,
+    int G, int Nr, int32_t* __restrict__ start) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<int64_t>(G + 1) * Nr) return;
+  const int g = static_cast<int>(i / Nr), e = static_cast<int>(i % Nr);
+  const int first = full_offsets[e], n = full_offsets[e + 1] - first;
+  int lo = 0;
+  if (g == G) {
+    lo = n;
+  } else {
+    const int64_t key = static_cast<int64_t>(g) * S;   // first token of group g
+    int hi = n;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (full_row_token[first + mid] < key) lo = mid + 1; else hi = mid;
+    }
   }
+  start[i] = lo;
+}
+
+constexpr int kCapScanThreads = 1024;
+
+// One workgroup: exclusive scan of kept(e, g) over the N_r*G entries in
+// (e, g) order, each thread a contiguous run of entries; wavefront prefix
+// sums by shuffles, then the 16 wavefront totals.
+__global__ __launch_bounds__(kCapScanThreads) void cap_scan_kernel(
+    const int32_t* __restrict__ start, int G, int Nr, int C, int32_t* __restrict__ base,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
+  constexpr int W = kCapScanThreads / kWave;
+  __shared__ int wsum[W], wpre[W];
+  __shared__ int offs[kMaxExperts + 1];
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int64_t M = static_cast<int64_t>(Nr) * G;
+  const int64_t per = (M + kCapScanThreads - 1) / kCapScanThreads;
+  const int64_t i0 = min(M, per * threadIdx.x), i1 = min(M, i0 + per);
+  auto kept = [&](int64_t i) {
+    const int e = static_cast<int>(i / G), g = static_cast<int>(i % G);
+    return min(start[static_cast<int64_t>(g + 1) * Nr + e] - start[static_cast<int64_t>(g) * Nr + e], C);
+  };
+  int s = 0;
+  for (int64_t i = i0; i < i1; ++i) s += kept(i);
+  int incl = s;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += y;
+  }
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    const int w = lane < W ? wsum[lane] : 0;
+    int wi = w;
+#pragma unroll
+    for (int o = 1; o < W; o <<= 1) {
+      const int y = __shfl_up(wi, o, kWave);
+      if (lane >= o) wi += y;
+    }
+    if (lane < W) wpre[lane] = wi - w;
+    if (lane == W - 1) offs[Nr] = wi;
+  }
+  __syncthreads();
+  int run = wpre[wave] + incl - s;
+  for (int64_t i = i0; i < i1; ++i) {
+    if (i % G == 0) offs[i / G] = run;
+    base[i] = run;
+    run += kept(i);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < Nr; e += kCapScanThreads) {
+    offsets[e] = offs[e];
+    counts[e] = offs[e + 1] - offs[e];
+  }
+  if (threadIdx.x == 0) offsets[Nr] = offs[Nr];
+}
+
+__global__ __launch_bounds__(256) void cap_scatter_kernel(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ full_slot_row,
+    const int32_t* __restrict__ full_offsets, const int32_t* __restrict__ start,
+    const int32_t* __restrict__ base, int64_t P, int K, int Nr, int S, int G, int C,
+    int32_t* __restrict__ row_token, int32_t* __restrict__ slot_row) {
+  const int64_t a = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (a >= P) return;
+  const int e = idx[a];
+  const int64_t t = a / K;
+  const int g = static_cast<int>(t / S);
+  const int q = full_slot_row[a] - full_offsets[e] - start[static_cast<int64_t>(g) * Nr + e];
+  if (q < C) {
+    const int row = base[static_cast<int64_t>(e) * G + g] + q;
+    slot_row[a] = row;
+    row_token[row] = static_cast<int32_t>(t);
+  } else {
+    slot_row[a] = -1;
+  }
+}
+
+// x_perm[r] = x[row_token[r]] for the rows below offsets[N_r] (read on the
+// device): one wavefront per row, 16 bytes per lane.
+__global__ __launch_bounds__(256) void gather_rows_kernel(
+    const int32_t* __restrict__ row_token, const int32_t* __restrict__ total, int64_t P,
+    const uint4* __restrict__ x, int chunks_per_row, uint4* __restrict__ x_perm) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * (256 / kWave) + threadIdx.x / kWave;
+  if (r >= P || r >= *total) return;
+  const uint4* src = x + static_cast<int64_t>(row_token[r]) * chunks_per_row;
+  uint4* dst = x_perm + r * chunks_per_row;
+  for (int c = lane; c < chunks_per_row; c += kWave) dst[c] = src[c];
+}
+
+hipError_t launch_dropless(const PermuteArgs& a, hipStream_t s) {
   if (a.T <= kSmallTokens && a.x_perm == nullptr) {
     hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(kSmallTokens), 0, s, a.topk_idx, a.T,
                        a.top_k, a.n_routed, a.counts, a.offsets, a.row_token, a.slot_row);
@@ -226,6 +341,48 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
                        static_cast<uint4*>(a.x_perm));
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
+  if (a.T == 0) {
+    // Empty batch: all counts and offsets are zero.
+    hipError_t err = launch_zero(a.counts, sizeof(int32_t) * a.n_routed, s);
+    if (err != hipSuccess) return err;
+    return launch_zero(a.offsets, sizeof(int32_t) * (a.n_routed + 1), s);
+  }
+  if (a.capacity <= 0) return launch_dropless(a, s);
+
+  PermuteArgs f = a;
+  f.counts = a.full_counts;
+  f.offsets = a.full_offsets;
+  f.row_token = a.full_row_token;
+  f.slot_row = a.full_slot_row;
+  f.x_perm = nullptr;
+  hipError_t err = launch_dropless(f, s);
+  if (err != hipSuccess) return err;
+  const int G = a.n_groups, Nr = a.n_routed;
+  const int64_t nb = (static_cast<int64_t>(G + 1) * Nr + 255) / 256;
+  hipLaunchKernelGGL(cap_bounds_kernel, dim3(static_cast<unsigned>(nb)), dim3(256), 0, s,
+                     a.full_row_token, a.full_offsets, a.group_len, G, Nr, a.group_start);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(cap_scan_kernel, dim3(1), dim3(kCapScanThreads), 0, s, a.group_start, G, Nr,
+                     a.capacity, a.group_base, a.counts, a.offsets);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  const int64_t P = static_cast<int64_t>(a.T) * a.top_k;
+  hipLaunchKernelGGL(cap_scatter_kernel, dim3(static_cast<unsigned>((P + 255) / 256)), dim3(256), 0,
+                     s, a.topk_idx, a.full_slot_row, a.full_offsets, a.group_start, a.group_base, P,
+                     a.top_k, Nr, a.group_len, G, a.capacity, a.row_token, a.slot_row);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (a.x_perm != nullptr) {
+    const int chunks = static_cast<int>((static_cast<int64_t>(a.d) * a.elt_bytes) / 16);
+    hipLaunchKernelGGL(gather_rows_kernel, dim3(static_cast<unsigned>((P + 3) / 4)), dim3(256), 0, s,
+                       a.row_token, a.offsets + Nr, P, static_cast<const uint4*>(a.x), chunks,
+                       static_cast<uint4*>(a.x_perm));
+    err = hipGetLastError();
+  }
+  return err;
 }
 
 }  // namespace moe

@@ -1,7 +1,8 @@
 // Grouped fp32 expert GEMMs (layers stored in float32).
 //
 // Same contract as the bf16 path (see GemmArgs): one thread per output
-// element, its group found by binary search in offsets, dot products
+// element over rows_total rows, its group found by binary search in offsets
+// (rows between offsets[n_groups] and extra_base are skipped), dot products
 // accumulated in fp32 in ascending k.  fp32 layers here are the small
 // parity-sized ones, so this path favours plainness over speed.
 #include "common.h"
@@ -39,6 +40,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(GemmArgs p) {
       if (MODE == kGateUp) b1 = static_cast<const float*>(p.Bx1) + s * p.bx_group_stride + n * p.ldb;
       arow = p.gather ? (r - p.extra_base) % p.extra_rows : r;
     } else {
+      // Rows past the last group's end (the rows an expert capacity dropped,
+      // below extra_base) hold no assignment and no valid gather index.
+      if (p.offsets != nullptr && r >= p.offsets[p.n_groups]) continue;
       const int g = p.offsets ? find_group(p.offsets, p.n_groups, r) : 0;
       b0 = static_cast<const float*>(p.B0) + g * p.b_group_stride + n * p.ldb;
       if (MODE == kGateUp) b1 = static_cast<const float*>(p.B1) + g * p.b_group_stride + n * p.ldb;

@@ -54,6 +54,16 @@ struct PermuteArgs {
   int32_t* block_counts;    // ws: [NB, N_r]
   int32_t* block_base;      // ws: [NB, N_r]
   int32_t* local_rank;      // ws: [P]
+  // Expert capacity (capacity > 0): at most `capacity` assignments per expert
+  // in every group of `group_len` consecutive tokens (n_groups groups).  The
+  // dropless dispatch goes to the full_* buffers first.
+  int capacity, group_len, n_groups;
+  int32_t* full_counts;     // ws: [N_r]
+  int32_t* full_offsets;    // ws: [N_r + 1]
+  int32_t* full_row_token;  // ws: [P]
+  int32_t* full_slot_row;   // ws: [P]
+  int32_t* group_start;     // ws: [n_groups + 1, N_r]
+  int32_t* group_base;      // ws: [N_r, n_groups]
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
 
@@ -78,7 +88,9 @@ struct GemmArgs {
   int64_t b_bytes;         // bytes of one group's B0 (and of its B1) (< 4 GB)
   const int32_t* offsets;
   int n_groups;
-  int64_t rows_total;      // sum of group rows (host known: P or T)
+  int64_t rows_total;      // upper bound of the row space (host known: P or T, plus the
+                           // extra groups); with an expert capacity the groups end at
+                           // offsets[n_groups] <= P and rows up to extra_base are unused
   const void* A;
   int64_t lda;
   const int32_t* gather;

@@ -32,11 +32,14 @@ class Layer:
     d_ff_shared: int
     gate: str = "softmax_topk"
     dtype: str = "bf16"
+    capacity: int = 0       # slots per expert per token group; 0 = dropless
+    group_size: int = 0     # tokens per capacity group; 0 = the whole batch
 
     @classmethod
     def of(cls, cfg) -> "Layer":
         return cls(cfg.d_model, cfg.n_routed, cfg.n_shared, cfg.top_k, cfg.d_ff,
-                   cfg.d_ff_shared, cfg.gate, cfg.dtype)
+                   cfg.d_ff_shared, cfg.gate, cfg.dtype, getattr(cfg, "capacity", 0),
+                   getattr(cfg, "group_size", 0))
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -44,7 +47,8 @@ class Layer:
 
     def c(self) -> MoeLayer:
         return MoeLayer(self.d_model, self.n_routed, self.n_shared, self.top_k, self.d_ff,
-                        self.d_ff_shared, _GATE[self.gate], _DT[self.dtype][0])
+                        self.d_ff_shared, _GATE[self.gate], _DT[self.dtype][0], self.capacity,
+                        self.group_size)
 
 
 def _p(t):

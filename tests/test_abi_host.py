@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     L = _lib.lib()
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
     assert _lib.status_str(MOE_OK) == "ok"
     assert "workspace" in _lib.status_str(MOE_ERR_WORKSPACE_TOO_SMALL)
     assert L.moe_last_hip_error() == 0
@@ -76,6 +76,9 @@ def test_workspace_size_scales_with_tokens():
     (dict(dtype=MOE_F32, d_model=62), 8, MOE_ERR_UNSUPPORTED),
     (dict(dtype=MOE_F32, d_model=60, d_ff=36, d_ff_shared=36), 8, MOE_OK),
     (dict(n_shared=0, d_ff_shared=0), 8, MOE_OK),
+    (dict(capacity=-1), 8, MOE_ERR_INVALID_ARG),
+    (dict(group_size=-3), 8, MOE_ERR_INVALID_ARG),
+    (dict(capacity=5, group_size=64), 8, MOE_OK),
 ])
 def test_layer_validation(kw, T, want):
     st, _ = ws_size(layer(**kw), T)
@@ -98,6 +101,16 @@ def test_route_argument_errors():
     assert L.moe_route(None, 16, *args, None) == MOE_ERR_INVALID_ARG
     # T == 0 is a valid no-op and must not touch the GPU
     assert L.moe_route(ctypes.byref(lay), 0, P(FAKE), P(FAKE), None, P(FAKE), P(FAKE), None) == MOE_OK
+
+
+def test_capacity_workspace():
+    # The capacity path keeps the dropless dispatch and per-group tables.
+    _, base = ws_size(layer(), 4096)
+    _, one = ws_size(layer(capacity=100), 4096)
+    _, many = ws_size(layer(capacity=100, group_size=16), 4096)
+    P, Nr = 4096 * 6, 64
+    assert one >= base + 2 * P * 4 + (2 * Nr + 1) * 4
+    assert many - one >= (256 - 1) * 2 * Nr * 4
 
 
 def test_route_stats_argument_errors():

@@ -1,0 +1,148 @@
+"""GPU parity of the capacity-limited dispatch (expert capacity per token
+group) against the oracle: moe_permute bit for bit, moe_forward under the
+layer tolerances.  MoE-survey blog page, section 3 (GShard expert capacity,
+running counter, overflowed tokens, local group dispatching) and section 4
+(Switch capacity factor).  Every call goes through the C ABI."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _parity import check_y, host, prepare, upload
+from mixture_experts_layer_43_amd import ops
+from test_gpu_parity import MID, announce, cfg_of, run_forward, sample_tokens
+
+pytestmark = pytest.mark.gpu
+
+
+def with_capacity(cfg, factor, S=0):
+    C = oracle.capacity_for(cfg.tokens, cfg.n_routed, cfg.top_k, factor, S)
+    return cfg.with_(capacity=C, group_size=S)
+
+
+def check_dispatch(got, ref, x=None, inp=None):
+    counts, offsets, row_token, slot_row = ref[:4]
+    np.testing.assert_array_equal(host(got["counts"]), counts)
+    np.testing.assert_array_equal(host(got["offsets"]), offsets)
+    n = int(offsets[-1])
+    np.testing.assert_array_equal(host(got["row_token"])[:n], row_token)
+    np.testing.assert_array_equal(host(got["slot_row"]), slot_row)
+    if got.get("x_perm") is not None:
+        xp = got["x_perm"][:n]
+        assert torch.equal(xp, x[torch.from_numpy(row_token.astype(np.int64)).to(x.device)])
+
+
+PERMUTE = [("mid-ragged", 1.0, 0), ("mid-ragged", 0.5, 100), ("mid-ragged", 1.25, 256),
+           ("mid-smallm", 1.0, 0), ("mid-smallm", 0.8, 37), ("mid-many-tokens", 1.0, 333),
+           ("mid-gshard", 1.0, 0), ("mid-many-experts", 1.5, 64), ("16b-decode", 1.0, 0),
+           ("16b-decode", 2.0, 16)]
+
+
+@pytest.mark.parametrize("name,factor,S", PERMUTE, ids=[f"{n}-f{f}-S{S}" for n, f, S in PERMUTE])
+@pytest.mark.parametrize("copy", [False, True], ids=["index", "copy"])
+def test_permute_with_capacity_is_bit_exact(name, factor, S, copy):
+    cfg = with_capacity(cfg_of(name), factor, S)
+    announce(f"permute capacity {name} C={cfg.capacity} S={S} copy={copy}")
+    inp = prepare(cfg)
+    ref = oracle.forward(cfg, inp, tokens=[0])
+    d = upload(inp)
+    lay = ops.Layer.of(cfg)
+    idx = torch.from_numpy(ref["topk_idx"]).to("cuda")
+    got = ops.permute(lay, idx, d["x"] if copy else None)
+    torch.cuda.synchronize()
+    want = oracle.dispatch_capacity(ref["topk_idx"], cfg.n_routed, cfg.capacity, S)
+    check_dispatch(got, want, d["x"])
+    assert (host(got["slot_row"]) < 0).any() or factor >= 2.0
+
+
+FORWARD = [("mid-ragged", 1.0, 0), ("mid-ragged", 0.7, 128), ("mid-smallm", 1.0, 50),
+           ("mid-gshard", 1.0, 0), ("mid-gshard", 1.25, 200), ("mid-f32", 1.0, 0),
+           ("mid-medm", 1.0, 64), ("16b-decode", 1.0, 0)]
+
+
+@pytest.mark.parametrize("name,factor,S", FORWARD, ids=[f"{n}-f{f}-S{S}" for n, f, S in FORWARD])
+def test_forward_with_capacity_matches_oracle(name, factor, S):
+    cfg = with_capacity(cfg_of(name), factor, S)
+    announce(f"forward capacity {name} C={cfg.capacity} S={S}")
+    inp = prepare(cfg)
+    ref = oracle.forward(cfg, inp)
+    f = run_forward(cfg, upload(inp))
+    np.testing.assert_array_equal(host(f.counts), ref["counts"])
+    np.testing.assert_array_equal(host(f.offsets), ref["offsets"])
+    check_y(host(f.y), ref["y"], cfg.dtype)
+
+
+@pytest.mark.parametrize("factor", [1.0, 1.25])
+def test_gshard_zipf_full_size_with_capacity(factor):
+    """The skewed GShard-shaped layer at full size: the Zipf bias overloads the
+    low experts, so a capacity factor near 1 drops many assignments."""
+    cfg = with_capacity(cfg_of("gshard-zipf"), factor)
+    sample = sample_tokens(cfg.tokens)
+    announce(f"forward capacity gshard-zipf full size C={cfg.capacity}")
+    inp = prepare(cfg)
+    ref = oracle.forward(cfg, inp, tokens=np.asarray(sample))
+    assert (~ref["kept"]).sum() > 0
+    d = upload(inp)
+    f = run_forward(cfg, d)
+    np.testing.assert_array_equal(host(f.counts), ref["counts"])
+    check_y(host(f.y)[list(sample)], ref["y"], cfg.dtype)
+    del d, f
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("S,C", [(0, 3), (4, 3), (50, 1)])
+def test_forced_overflow(S, C):
+    """Every token chooses experts 5 and 11; beyond the first C tokens of a
+    group, tokens overflow and y = shared experts + residual."""
+    cfg = MID["mid-ragged"].with_(tokens=300, top_k=2, capacity=C, group_size=S, seed=700 + S)
+    inp = prepare(cfg)
+    bias = np.zeros(cfg.n_routed, np.float32)
+    bias[[5, 11]] = 40.0
+    inp["bias"] = bias
+    announce(f"forced overflow S={S} C={C}")
+    ref = oracle.forward(cfg, inp, residual=True)
+    d = upload(inp)
+    f = run_forward(cfg, d, residual=d["x"])
+    np.testing.assert_array_equal(host(f.counts), ref["counts"])
+    check_y(host(f.y), ref["y"], cfg.dtype)
+
+
+def test_capacity_without_drops_equals_dropless_bitwise():
+    cfg = MID["mid-many-tokens"]
+    announce("capacity >= T and one-token groups vs dropless")
+    inp = prepare(cfg)
+    d = upload(inp)
+    y0 = run_forward(cfg, d).y.clone()
+    for kw in (dict(capacity=cfg.tokens), dict(capacity=1, group_size=1)):
+        y1 = run_forward(cfg.with_(**kw), d).y
+        assert torch.equal(y0, y1), kw
+
+
+def test_combine_skips_dropped_slots():
+    """moe_combine alone with some slot_row entries -1 (and garbage in the
+    rows they would name) adds nothing for them."""
+    cfg = MID["mid-ragged"].with_(tokens=64, seed=720)
+    announce("combine with dropped slots")
+    lay = ops.Layer.of(cfg)
+    T, K, dm = cfg.tokens, cfg.top_k, cfg.d_model
+    g = torch.Generator().manual_seed(3)
+    y_perm = torch.randn(T * K, dm, generator=g).to(torch.bfloat16)
+    slot = torch.randperm(T * K, generator=g).to(torch.int32)
+    w = torch.rand(T, K, generator=g)
+    drop = (torch.rand(T * K, generator=g) < 0.3) | (slot == 0)   # row 0 is only read in place of a dropped row
+    slot_d = torch.where(drop, torch.full_like(slot, -1), slot)
+    y_perm_nan = y_perm.clone()
+    y_perm_nan[0] = float("nan")
+    out = ops.combine(lay, y_perm_nan.cuda(), slot_d.cuda(), w.cuda())
+    torch.cuda.synchronize()
+    ref = np.zeros((T, dm))
+    yp = y_perm_nan.float().numpy().astype(np.float64)
+    for t in range(T):
+        for j in range(K):
+            s = int(slot_d[t * K + j])
+            if s >= 0:
+                ref[t] += float(w[t, j]) * yp[s]
+    assert np.isfinite(host(out)).all()
+    check_y(host(out), ref, "bf16")
