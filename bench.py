@@ -25,6 +25,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import dataclasses
 import json
 import os
 import sys
@@ -216,6 +217,18 @@ def main():
     route_ms = per_call_ms(route_plain)
     route_stats_ms = per_call_ms(route_with_stats)
 
+    # Expert capacity (Switch/GShard, one group of the whole batch): the same
+    # layer with C = ceil(factor * T * K' / N_r) slots per expert.
+    capacity = {}
+    for factor in (1.0, 1.25):
+        C = -(-int(factor * 100) * cfg.tokens * cfg.top_k // (100 * cfg.n_routed))
+        fc = ops.Forward(dataclasses.replace(lay, capacity=C), cfg.tokens, dev)
+        ms_c = per_call_ms(lambda: fc(*call_args, checked=True), n=max(3, min(args.steps, 10)))
+        capacity[str(factor)] = {"capacity": C, "ms_per_step": ms_c,
+                                 "kept_frac": int(fc.counts.sum()) / (cfg.tokens * cfg.top_k)}
+        del fc
+        torch.cuda.empty_cache()
+
     T, dm, I, K = cfg.tokens, cfg.d_model, cfg.d_ff, cfg.top_k
     P = T * K
     # With I_s == I the shared experts run as K_s extra groups of T rows in
@@ -282,6 +295,7 @@ def main():
         "stage_ms": st,
         "routing_stats": {"route_ms": route_ms, "route_stats_ms": route_stats_ms,
                           "n_devices": n_dev},
+        "capacity": capacity,
         "layer_algorithmic_bytes": layer_bytes,
         "layer_hbm_gbs": layer_gbs,
         "layer_hbm_frac": layer_gbs / PEAK_HBM_GBS,
