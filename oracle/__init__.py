@@ -14,6 +14,8 @@ from .moe import (  # noqa: F401
     decode,
     dispatch,
     expert_ffn,
+    ffn_of,
+    relu_ffn,
     forward,
     gate_values,
     route,

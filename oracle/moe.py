@@ -19,7 +19,9 @@ Readings taken where the pages leave a step open:
     centroid (eq. 10-11 index the gates from K_s+1).
   * "softmax_topk" gates are s_i on the chosen experts, not renormalised
     (eq. 10); "topk_softmax" is Softmax(KeepTopK(z, K')) with no noise.
-  * expert FFN is the SiLU-gated form W2 (silu(W1 u) * (W3 u)).
+  * expert FFN is the SiLU-gated form W2 (silu(W1 u) * (W3 u)); with
+    cfg.ffn == "relu" it is GShard's wo ReLU(wi u) ([P4] section 3), with
+    wi in the w_gate slot and wo in the w_down slot.
   * top-k ties break toward the lower expert id; chosen ids are reported
     in ascending order.
   * shared experts enter with weight 1 (eq. 9, first sum); the residual
@@ -123,11 +125,27 @@ def expert_ffn(X: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.n
     return (silu(X @ w_gate.T) * (X @ w_up.T)) @ w_down.T
 
 
-def shared_ffn(X: np.ndarray, ws_gate, ws_up, ws_down) -> np.ndarray:
+def relu_ffn(X: np.ndarray, wi: np.ndarray, wo: np.ndarray) -> np.ndarray:
+    """GShard's position-wise FFN_e(x) = wo ReLU(wi x) ([P4] section 3) on the
+    rows of X.  wi [I, d]; wo [d, I]."""
+    return np.maximum(X @ wi.T, 0.0) @ wo.T
+
+
+def ffn_of(kind: str, X, w_gate, w_up, w_down):
+    """One expert of either form: SiLU-gated (three matrices) or ReLU (wi =
+    w_gate, wo = w_down)."""
+    if kind == "relu":
+        return relu_ffn(X, w_gate, w_down)
+    if kind == "silu":
+        return expert_ffn(X, w_gate, w_up, w_down)
+    raise ValueError(f"unknown ffn {kind!r}")
+
+
+def shared_ffn(X: np.ndarray, ws_gate, ws_up, ws_down, ffn: str = "silu") -> np.ndarray:
     """Sum over the K_s shared experts, each with weight 1 ([P1] eq. 9, first sum)."""
     y = np.zeros((X.shape[0], X.shape[1]), dtype=np.float64)
     for s in range(ws_gate.shape[0]):
-        y += expert_ffn(X, ws_gate[s], ws_up[s], ws_down[s])
+        y += ffn_of(ffn, X, ws_gate[s], None if ws_up is None else ws_up[s], ws_down[s])
     return y
 
 
@@ -143,6 +161,7 @@ def forward(cfg, inputs: dict, tokens=None, residual: bool = False) -> dict:
     b = None if inputs.get("bias") is None else np.asarray(inputs["bias"], dtype=np.float64)
     T, d = x.shape
     Nr, k = cfg.n_routed, cfg.top_k
+    kind = getattr(cfg, "ffn", "silu")
 
     z = router_logits(x, wr, b)
     idx, g = route(z, k, cfg.gate)
@@ -169,13 +188,14 @@ def forward(cfg, inputs: dict, tokens=None, residual: bool = False) -> dict:
         toks = toks[want]
         slots = np.nonzero(idx[toks] == e)[1]   # rows hold kept assignments only
         ge = g[toks, slots]
-        F = expert_ffn(x[toks], decode(inputs["w_gate"][e], dt),
-                       decode(inputs["w_up"][e], dt), decode(inputs["w_down"][e], dt))
+        w_up = inputs.get("w_up")
+        F = ffn_of(kind, x[toks], decode(inputs["w_gate"][e], dt),
+                   None if w_up is None else decode(w_up[e], dt), decode(inputs["w_down"][e], dt))
         y[pos[toks]] += ge[:, None] * F
 
     if cfg.n_shared > 0:
-        y += shared_ffn(x[sel], decode(inputs["ws_gate"], dt),
-                        decode(inputs["ws_up"], dt), decode(inputs["ws_down"], dt))
+        y += shared_ffn(x[sel], decode(inputs["ws_gate"], dt), decode(inputs.get("ws_up"), dt),
+                        decode(inputs["ws_down"], dt), kind)
     if residual:
         y += x[sel]
 

@@ -36,6 +36,7 @@ class LayerConfig:
     zipf_s: float = 0.0        # > 0: per-expert router bias -s*ln(e+1)
     seed: int = 4300
     gap: float = 1e-3          # min logit gap between the K'-th and (K'+1)-th
+    ffn: str = "silu"          # "silu": W2 (silu(W1 u) * (W3 u)); "relu": wo ReLU(wi u) (W1, W2)
     capacity: int = 0          # > 0: assignments kept per expert per token group; 0 = dropless
     group_size: int = 0        # tokens per group for the capacity (0 = the whole batch)
 

@@ -123,6 +123,9 @@ def make_inputs(cfg: LayerConfig, seed: int | None = None, experts: bool = True)
                 ("ws_up", 6, (Ks, Is, d), 1.0 / np.sqrt(d)),
                 ("ws_down", 7, (Ks, d, Is), 1.0 / np.sqrt(Is)),
             ):
+                if cfg.ffn == "relu" and name in ("w_up", "ws_up"):
+                    out[name] = None          # the ReLU FFN has two matrices
+                    continue
                 a = np.empty(shape, dtype=sdt)
                 _fill_experts(a, std, seed, tensor, cfg.dtype, pool)
                 out[name] = a

@@ -27,6 +27,12 @@ def _ffn(u, w1, w3, w2):
     return [_dot(row, h) for row in w2]
 
 
+def _ffn_relu(u, wi, wo):
+    # GShard position-wise FFN: wo . ReLU(wi . u)
+    h = [max(0.0, _dot(r, u)) for r in wi]
+    return [_dot(row, h) for row in wo]
+
+
 def _gates(z, k, gate):
     n = len(z)
     g = [0.0] * n
@@ -50,7 +56,7 @@ def _gates(z, k, gate):
 
 
 def brute_forward(x, w_router, bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
-                  top_k, gate, residual=False, capacity=0, group_size=0):
+                  top_k, gate, residual=False, capacity=0, group_size=0, ffn="silu"):
     """All arguments are nested Python lists of floats (bias may be None).
 
     capacity > 0: each expert takes at most `capacity` tokens per group of
@@ -58,7 +64,13 @@ def brute_forward(x, w_router, bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_do
     served in token order; a token that finds a chosen expert full loses that
     expert's gate (MoE-survey blog page, section 3, expert capacity).
 
+    ffn "relu": every expert is wo . ReLU(wi . u) with wi = w_gate, wo = w_down
+    (w_up unused; MoE-survey blog page, section 3).
+
     Returns (chosen ids per token, ascending; dense gates per token; y)."""
+    def expert(u, w1, w3, w2):
+        return _ffn_relu(u, w1, w2) if ffn == "relu" else _ffn(u, w1, w3, w2)
+
     chosen_all, g_all, y_all = [], [], []
     n = len(w_router)
     S = group_size if 0 < group_size < len(x) else len(x)
@@ -75,11 +87,11 @@ def brute_forward(x, w_router, bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_do
                     g[i] = 0.0
         y = [0.0] * len(u)
         for i in range(n):                       # dense: every routed expert
-            f = _ffn(u, w_gate[i], w_up[i], w_down[i])
+            f = expert(u, w_gate[i], None if w_up is None else w_up[i], w_down[i])
             for c in range(len(u)):
                 y[c] += g[i] * f[c]
         for s in range(len(ws_gate)):            # shared experts, gate 1
-            f = _ffn(u, ws_gate[s], ws_up[s], ws_down[s])
+            f = expert(u, ws_gate[s], None if ws_up is None else ws_up[s], ws_down[s])
             for c in range(len(u)):
                 y[c] += f[c]
         if residual:

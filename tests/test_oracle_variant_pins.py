@@ -1,0 +1,97 @@
+"""Pins of the oracle's gate and FFN variants.
+
+GShard's position-wise ReLU FFN, FFN_e(x) = wo ReLU(wi x) (MoE-survey blog
+page, section 3).  Checked against the dense pure-Python brute force, the
+split identity of the intermediate dimension (DeepSeekMoE page, section 3.1,
+which holds for any FFN that acts element-wise on the intermediate), and
+closed forms where the ReLU is the identity or zero.  Planted mistakes
+close the file.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.moe as om
+from _brute import brute_forward
+from synth import LayerConfig, make_inputs
+
+
+def cfg_of(**kw):
+    base = dict(name="variant", tokens=10, d_model=6, n_routed=5, n_shared=1, top_k=2, d_ff=4,
+                d_ff_shared=3, dtype="f32", seed=931, gap=1e-3, ffn="relu")
+    base.update(kw)
+    return LayerConfig(**base)
+
+
+def inputs(cfg):
+    inp = make_inputs(cfg)
+    oracle.enforce_gap(cfg, inp)
+    return inp
+
+
+RELU_CASES = [dict(), dict(gate="topk_softmax"), dict(n_shared=0, top_k=1), dict(n_shared=2, top_k=3),
+              dict(zipf_s=1.2, capacity=3)]
+
+
+@pytest.mark.parametrize("kw", RELU_CASES, ids=[str(c) for c in RELU_CASES])
+def test_relu_layer_matches_dense_brute_force(kw):
+    cfg = cfg_of(**kw)
+    inp = inputs(cfg)
+    assert inp["w_up"] is None and inp["ws_up"] is None
+    L = {k: (None if v is None else np.asarray(v, np.float64).tolist()) for k, v in inp.items()}
+    _, _, y = brute_forward(L["x"], L["w_router"], L["bias"], L["w_gate"], None, L["w_down"],
+                            L["ws_gate"], None, L["ws_down"], cfg.top_k, cfg.gate, True,
+                            cfg.capacity, cfg.group_size, ffn="relu")
+    np.testing.assert_allclose(om.forward(cfg, inp, residual=True)["y"], np.array(y),
+                               rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("m", [2, 4])
+def test_relu_split_identity(m):
+    rng = np.random.default_rng(5)
+    X, wi, wo = rng.normal(size=(7, 6)), rng.normal(size=(8, 6)), rng.normal(size=(6, 8))
+    whole = om.relu_ffn(X, wi, wo)
+    parts = sum(om.relu_ffn(X, wi[j::m], wo[:, j::m]) for j in range(m))
+    np.testing.assert_allclose(parts, whole, rtol=1e-13, atol=1e-13)
+
+
+def test_relu_identity_and_zero_regions():
+    # Non-negative x and wi: every pre-activation is >= 0, ReLU is the identity
+    # and the FFN is the linear map wo wi.  With wi <= 0 it is exactly zero.
+    rng = np.random.default_rng(6)
+    X, wi, wo = np.abs(rng.normal(size=(5, 4))), np.abs(rng.normal(size=(3, 4))), rng.normal(size=(4, 3))
+    np.testing.assert_allclose(om.relu_ffn(X, wi, wo), X @ (wo @ wi).T, rtol=1e-13)
+    assert not om.relu_ffn(X, -wi, wo).any()
+
+
+def test_relu_expert_rows_closed_form():
+    # One token, one hidden unit per expert: FFN(x) = wo * max(0, wi . x).
+    x = np.array([[1.0, -2.0, 0.5]])
+    wi = np.array([[0.5, 0.25, 2.0]])      # wi . x = 0.5 - 0.5 + 1.0 = 1.0
+    wo = np.array([[3.0], [-1.0], [0.0]])
+    np.testing.assert_array_equal(om.relu_ffn(x, wi, wo), [[3.0, -1.0, 0.0]])
+    np.testing.assert_array_equal(om.relu_ffn(x, -wi, wo), [[0.0, 0.0, 0.0]])
+
+
+# --- planted mistakes --------------------------------------------------------
+MISTAKES = {
+    "relu after wo": lambda X, wi, wo: np.maximum(X @ wi.T @ wo.T, 0.0),
+    "silu instead of relu": lambda X, wi, wo: om.silu(X @ wi.T) @ wo.T,
+    "leaky": lambda X, wi, wo: np.where(X @ wi.T > 0, X @ wi.T, 0.01 * (X @ wi.T)) @ wo.T,
+}
+PINS = [lambda: [test_relu_layer_matches_dense_brute_force(c) for c in RELU_CASES],
+        test_relu_identity_and_zero_regions, test_relu_expert_rows_closed_form]
+
+
+@pytest.mark.parametrize("name", sorted(MISTAKES))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    monkeypatch.setattr(om, "relu_ffn", MISTAKES[name])
+    failed = 0
+    for pin in PINS:
+        try:
+            pin()
+        except AssertionError:
+            failed += 1
+    assert failed > 0, f"planted mistake {name!r} passed every pin"
