@@ -19,6 +19,7 @@ from .moe import (  # noqa: F401
     forward,
     gate_values,
     route,
+    route_selection_bias,
     router_logits,
     select_topk,
     shared_ffn,

@@ -26,6 +26,10 @@ Readings taken where the pages leave a step open:
     in ascending order.
   * shared experts enter with weight 1 (eq. 9, first sum); the residual
     u_t of eq. 9 is added only when asked for.
+  * with cfg.bias_mode == "selection" the bias steers only the top-K'
+    choice and the gates come from the unbiased logits (the article that
+    describes the bias does not say whether it enters the gate value);
+    "logits" (default) adds it before both.
   * with cfg.capacity > 0 the dispatch keeps at most that many assignments
     per expert and token group ([P4] section 3, expert capacity; readings in
     oracle/capacity.py) and a dropped assignment contributes nothing.
@@ -97,6 +101,15 @@ def route(z: np.ndarray, k: int, gate: str):
     return idx.astype(np.int32), gate_values(z, idx, gate)
 
 
+def route_selection_bias(z: np.ndarray, bias: np.ndarray, k: int, gate: str):
+    """Selection-only bias: the top-K' is taken on z + b (a per-expert bias that
+    steers the load, the balancing without an auxiliary loss of the Tencent
+    Cloud "DeepSeek MoE" article), the gate values on the unbiased z.  z are
+    the logits without the bias."""
+    idx, _ = route(z + bias[None, :], k, gate)
+    return idx, gate_values(z, idx, gate)
+
+
 def dispatch(idx: np.ndarray, n_routed: int):
     """Per-expert token lists for evaluating only the chosen experts ([P4] sec. 2).
 
@@ -163,8 +176,12 @@ def forward(cfg, inputs: dict, tokens=None, residual: bool = False) -> dict:
     Nr, k = cfg.n_routed, cfg.top_k
     kind = getattr(cfg, "ffn", "silu")
 
-    z = router_logits(x, wr, b)
-    idx, g = route(z, k, cfg.gate)
+    if getattr(cfg, "bias_mode", "logits") == "selection" and b is not None:
+        z = router_logits(x, wr)
+        idx, g = route_selection_bias(z, b, k, cfg.gate)
+    else:
+        z = router_logits(x, wr, b)
+        idx, g = route(z, k, cfg.gate)
     cap = getattr(cfg, "capacity", 0)
     if cap > 0:
         # Expert capacity ([P4] section 3): dropped assignments get gate 0.

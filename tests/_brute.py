@@ -56,13 +56,17 @@ def _gates(z, k, gate):
 
 
 def brute_forward(x, w_router, bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
-                  top_k, gate, residual=False, capacity=0, group_size=0, ffn="silu"):
+                  top_k, gate, residual=False, capacity=0, group_size=0, ffn="silu",
+                  bias_mode="logits"):
     """All arguments are nested Python lists of floats (bias may be None).
 
     capacity > 0: each expert takes at most `capacity` tokens per group of
     `group_size` consecutive tokens (0: the whole batch), first come first
     served in token order; a token that finds a chosen expert full loses that
     expert's gate (MoE-survey blog page, section 3, expert capacity).
+
+    bias_mode "selection": the bias takes part in choosing the experts only;
+    the gate values come from the logits without it.
 
     ffn "relu": every expert is wo . ReLU(wi . u) with wi = w_gate, wo = w_down
     (w_up unused; MoE-survey blog page, section 3).
@@ -78,6 +82,14 @@ def brute_forward(x, w_router, bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_do
     for t, u in enumerate(x):
         z = [_dot(w_router[i], u) + (bias[i] if bias is not None else 0.0) for i in range(n)]
         chosen, g = _gates(z, top_k, gate)
+        if bias_mode == "selection" and bias is not None:
+            z0 = [_dot(w_router[i], u) for i in range(n)]
+            _, g0 = _gates(z0, n, gate)            # gates of every expert, unbiased
+            if gate == "topk_softmax":
+                m = max(z0[i] for i in chosen)
+                tot = sum(math.exp(z0[i] - m) for i in chosen)
+                g0 = [math.exp(z0[i] - m) / tot if i in chosen else 0.0 for i in range(n)]
+            g = [g0[i] if i in chosen else 0.0 for i in range(n)]
         if capacity > 0:
             for i in chosen:
                 key = (t // S, i)

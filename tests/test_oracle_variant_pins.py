@@ -95,3 +95,72 @@ def test_planted_mistake_is_caught(name, monkeypatch):
         except AssertionError:
             failed += 1
     assert failed > 0, f"planted mistake {name!r} passed every pin"
+
+
+# --- selection-only bias ------------------------------------------------------
+SEL_CASES = [dict(ffn="silu", zipf_s=1.2, bias_mode="selection"),
+             dict(ffn="silu", zipf_s=1.2, bias_mode="selection", gate="topk_softmax"),
+             dict(ffn="relu", zipf_s=2.0, bias_mode="selection", top_k=1, n_shared=0)]
+
+
+@pytest.mark.parametrize("kw", SEL_CASES, ids=[str(c) for c in SEL_CASES])
+def test_selection_bias_matches_dense_brute_force(kw):
+    cfg = cfg_of(**kw)
+    inp = inputs(cfg)
+    L = {k: (None if v is None else np.asarray(v, np.float64).tolist()) for k, v in inp.items()}
+    chosen, g, y = brute_forward(L["x"], L["w_router"], L["bias"], L["w_gate"], L.get("w_up"),
+                                 L["w_down"], L["ws_gate"], L.get("ws_up"), L["ws_down"], cfg.top_k,
+                                 cfg.gate, False, ffn=cfg.ffn, bias_mode="selection")
+    r = om.forward(cfg, inp)
+    np.testing.assert_array_equal(r["topk_idx"], np.array(chosen))
+    np.testing.assert_allclose(r["y"], np.array(y), rtol=1e-12, atol=1e-12)
+    dense = np.zeros((cfg.tokens, cfg.n_routed))
+    dense[np.arange(cfg.tokens)[:, None], r["topk_idx"]] = r["topk_w"]
+    np.testing.assert_allclose(dense, np.array(g), rtol=1e-12, atol=0)
+
+
+def test_selection_bias_forced_experts_closed_form():
+    """A bias of 40 on experts 1 and 3 makes every token choose them; with the
+    bias in the logits their softmax_topk gates are ~1/2 each and sum to ~1,
+    with a selection-only bias they are the unbiased s_1, s_3."""
+    cfg = cfg_of(ffn="silu", bias_mode="selection", tokens=8)
+    inp = inputs(cfg)
+    bias = np.zeros(cfg.n_routed)
+    bias[[1, 3]] = 40.0
+    z = om.router_logits(inp["x"].astype(np.float64), inp["w_router"].astype(np.float64))
+    idx, g = om.route_selection_bias(z, bias, 2, "softmax_topk")
+    assert (idx == [1, 3]).all()
+    s = np.exp(z - z.max(1, keepdims=True))
+    s /= s.sum(1, keepdims=True)
+    np.testing.assert_allclose(g, s[:, [1, 3]], rtol=1e-14)
+    _, gl = om.route(z + bias, 2, "softmax_topk")
+    assert np.all(np.abs(gl.sum(1) - 1) < 1e-12) and np.all(g.sum(1) < 0.99)
+
+
+def test_zero_bias_is_the_plain_route():
+    rng = np.random.default_rng(8)
+    z = rng.normal(size=(20, 7))
+    for gate in ("softmax_topk", "topk_softmax"):
+        a, b = om.route(z, 3, gate), om.route_selection_bias(z, np.zeros(7), 3, gate)
+        np.testing.assert_array_equal(a[0], b[0])
+        np.testing.assert_array_equal(a[1], b[1])
+
+
+SEL_MISTAKES = {
+    "gates from biased logits": lambda z, b, k, gate: om.route(z + b[None, :], k, gate),
+    "selection ignores bias": lambda z, b, k, gate: om.route(z, k, gate),
+}
+SEL_PINS = [lambda: [test_selection_bias_matches_dense_brute_force(c) for c in SEL_CASES],
+            test_selection_bias_forced_experts_closed_form]
+
+
+@pytest.mark.parametrize("name", sorted(SEL_MISTAKES))
+def test_planted_selection_mistake_is_caught(name, monkeypatch):
+    monkeypatch.setattr(om, "route_selection_bias", SEL_MISTAKES[name])
+    failed = 0
+    for pin in SEL_PINS:
+        try:
+            pin()
+        except AssertionError:
+            failed += 1
+    assert failed > 0, f"planted mistake {name!r} passed every pin"
