@@ -57,13 +57,36 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = 1,          /* null required pointer, T < 0, bad enum, K' out of range,
-                                       negative capacity or group_size                          */
+                                       negative capacity or group_size, bad ffn or bias_mode     */
   MOE_ERR_UNSUPPORTED = 2,          /* shape/alignment outside the supported set above         */
   MOE_ERR_WORKSPACE_TOO_SMALL = 3,  /* ws_bytes below moe_workspace_size()                      */
   MOE_ERR_HIP = 4                   /* a HIP launch or query failed                              */
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Expert FFN form. */
+typedef enum {
+  /* W2 (silu(W1 u) * (W3 u)): w_gate = W1, w_up = W3, w_down = W2.       */
+  MOE_FFN_SILU_GATED = 0,
+  /* wo ReLU(wi u), GShard's position-wise FFN (MoE-survey blog page,
+     section 3): w_gate = wi, w_down = wo; w_up and ws_up are not read
+     (NULL allowed).                                                      */
+  MOE_FFN_RELU = 1
+} moe_ffn;
+
+/* Where logit_bias enters. */
+typedef enum {
+  /* Added to the logits before both the selection and the gate values. */
+  MOE_BIAS_LOGITS = 0,
+  /* Selection only: the top-K' is taken on z + b, the gate values (and the
+     routing statistics) use the unbiased z.  This is the per-expert bias of
+     the load balancing without an auxiliary loss in the Tencent Cloud
+     article "DeepSeek MoE: innovations and breakthroughs of the mixture-of-
+     experts architecture" (section on auxiliary-loss-free balancing), which
+     leaves the gate values unstated.                                      */
+  MOE_BIAS_SELECTION = 1
+} moe_bias_mode;
 
 typedef enum {
   /* g_i = s_i on the top-K' of s = Softmax over N_r routed experts, not
@@ -97,6 +120,8 @@ typedef struct {
   int32_t dtype;        /* moe_dtype                          */
   int32_t capacity;     /* C, slots per expert per group; 0 = no limit */
   int32_t group_size;   /* S, tokens per capacity group; 0 = all T     */
+  int32_t ffn;          /* moe_ffn                                     */
+  int32_t bias_mode;    /* moe_bias_mode                               */
 } moe_layer;
 
 int moe_abi_version(void);

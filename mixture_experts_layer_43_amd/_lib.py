@@ -10,6 +10,8 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
 MOE_GATE_SOFTMAX_TOPK, MOE_GATE_TOPK_SOFTMAX = 0, 1
+MOE_FFN_SILU_GATED, MOE_FFN_RELU = 0, 1
+MOE_BIAS_LOGITS, MOE_BIAS_SELECTION = 0, 1
 
 EXPORTS = (
     "moe_abi_version", "moe_status_str", "moe_last_hip_error", "moe_workspace_size",
@@ -24,7 +26,7 @@ STAGES = ("route", "dispatch", "routed_gate_up", "routed_down", "shared_gate_up"
 class MoeLayer(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "d_model", "n_routed", "n_shared", "top_k", "d_ff", "d_ff_shared", "gate", "dtype",
-        "capacity", "group_size")]
+        "capacity", "group_size", "ffn", "bias_mode")]
 
 
 class MoeError(RuntimeError):

@@ -97,6 +97,8 @@ int check_layer(const moe_layer* L, int64_t T) {
     return MOE_ERR_INVALID_ARG;
   if (L->n_shared > 0 && L->d_ff_shared <= 0) return MOE_ERR_INVALID_ARG;
   if (L->capacity < 0 || L->group_size < 0) return MOE_ERR_INVALID_ARG;
+  if (L->ffn != MOE_FFN_SILU_GATED && L->ffn != MOE_FFN_RELU) return MOE_ERR_INVALID_ARG;
+  if (L->bias_mode != MOE_BIAS_LOGITS && L->bias_mode != MOE_BIAS_SELECTION) return MOE_ERR_INVALID_ARG;
   if (L->top_k < 1 || L->top_k > L->n_routed || L->top_k > 16) return MOE_ERR_INVALID_ARG;
   if (L->n_routed > 256) return MOE_ERR_UNSUPPORTED;
   if (T >= (int64_t{1} << 31) / 16) return MOE_ERR_UNSUPPORTED;
@@ -143,6 +145,19 @@ int opt(const void* p) { return (p == nullptr || aligned16(p)) ? MOE_OK : MOE_ER
 
 char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
+// The first projection of an expert: silu(W1 u) * (W3 u), or for the ReLU
+// FFN ReLU(wi u) with wi in the W1 slot (one matrix, the plain GEMM with a
+// clamped epilogue).
+moe::GemmArgs first_projection(const moe_layer* L, moe::GemmArgs g) {
+  if (L->ffn == MOE_FFN_RELU) {
+    g.mode = moe::kDown;
+    g.relu = true;
+    g.B1 = nullptr;
+    g.Bx1 = nullptr;
+  }
+  return g;
+}
+
 moe::GemmArgs routed_gate_up(const moe_layer* L, int64_t T, const int32_t* offsets,
                              const void* A, const int32_t* gather, const void* w_gate,
                              const void* w_up, void* H) {
@@ -166,7 +181,7 @@ moe::GemmArgs routed_gate_up(const moe_layer* L, int64_t T, const int32_t* offse
   g.C = H;
   g.ldc = L->d_ff;
   g.mode = moe::kGateUp;
-  return g;
+  return first_projection(L, g);
 }
 
 moe::GemmArgs routed_down(const moe_layer* L, int64_t T, const int32_t* offsets, const void* H,
@@ -204,7 +219,7 @@ void add_shared_groups(const moe_layer* L, int64_t T, moe::GemmArgs& g, const vo
   g.extra_base = T * L->top_k;
   g.rows_total = forward_rows(L, T);
   g.Bx0 = b0;
-  g.Bx1 = b1;
+  g.Bx1 = L->ffn == MOE_FFN_RELU ? nullptr : b1;
   g.bx_group_stride = static_cast<int64_t>(L->d_ff_shared) * L->d_model;
   g.bx_bytes = g.bx_group_stride * e;
   if (down) g.a_bytes = g.rows_total * static_cast<int64_t>(L->d_ff) * e;
@@ -236,7 +251,7 @@ moe::GemmArgs shared_gate_up(const moe_layer* L, int64_t T, const void* x, const
   g.C = h_shared;
   g.ldc = wsh;
   g.mode = moe::kGateUp;
-  return g;
+  return first_projection(L, g);
 }
 
 // The down projection's K runs over the K_s matrices [d, I_s] in turn.
@@ -331,6 +346,7 @@ static moe::RouteArgs route_args(const moe_layer* layer, int64_t T, const void* 
   a.n_routed = layer->n_routed;
   a.top_k = layer->top_k;
   a.gate = layer->gate;
+  a.bias_sel = layer->bias_mode == MOE_BIAS_SELECTION;
   a.x_bf16 = layer->dtype == MOE_BF16;
   a.topk_idx = topk_idx;
   a.topk_w = topk_w;
@@ -431,7 +447,7 @@ int moe_expert_ffn(const moe_layer* layer, int64_t T, const int32_t* offsets, co
   MOE_TRY(need(offsets));
   MOE_TRY(needT(x_perm, T));
   MOE_TRY(need(w_gate));
-  MOE_TRY(need(w_up));
+  MOE_TRY(layer->ffn == MOE_FFN_SILU_GATED ? need(w_up) : opt(w_up));
   MOE_TRY(need(w_down));
   MOE_TRY(needT(y_perm, T));
   MOE_TRY(need(ws));
@@ -453,7 +469,7 @@ int moe_shared_ffn(const moe_layer* layer, int64_t T, const void* x, const void*
   if (layer->n_shared > 0) {
     MOE_TRY(needT(x, T));
     MOE_TRY(need(ws_gate));
-    MOE_TRY(need(ws_up));
+    MOE_TRY(layer->ffn == MOE_FFN_SILU_GATED ? need(ws_up) : opt(ws_up));
     MOE_TRY(need(ws_down));
   }
   const Layout lo = layout_of(layer, T);
@@ -507,11 +523,11 @@ static int forward_impl(const moe_layer* layer, int64_t T, const void* x,
   MOE_TRY(need(w_router));
   MOE_TRY(opt(logit_bias));
   MOE_TRY(need(w_gate));
-  MOE_TRY(need(w_up));
+  MOE_TRY(layer->ffn == MOE_FFN_SILU_GATED ? need(w_up) : opt(w_up));
   MOE_TRY(need(w_down));
   if (layer->n_shared > 0) {
     MOE_TRY(need(ws_gate));
-    MOE_TRY(need(ws_up));
+    MOE_TRY(layer->ffn == MOE_FFN_SILU_GATED ? need(ws_up) : opt(ws_up));
     MOE_TRY(need(ws_down));
   }
   MOE_TRY(opt(residual));

@@ -453,6 +453,8 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
         }
       }
   } else {
+    // ReLU FFN up projection: clamp at 0 (max with -inf leaves v as is).
+    const float lo = p.relu ? 0.0f : -INFINITY;
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -461,7 +463,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int r = wm * TM + i * 32 + 8 * (v >> 2) + hrow + (v & 3);
-          ct[cpos(r, c)] = f32_to_bf16(acc[i][j][v]);
+          ct[cpos(r, c)] = f32_to_bf16(fmaxf(acc[i][j][v], lo));
         }
       }
   }

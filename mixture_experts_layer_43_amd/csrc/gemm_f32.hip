@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(GemmArgs p) {
         const int64_t bo = static_cast<int64_t>(k / p.k_sub) * p.b_sub_stride + (k % p.k_sub);
         s0 = fmaf(a[k], b0[bo], s0);
       }
-      C[r * p.ldc + n] = s0;
+      C[r * p.ldc + n] = p.relu ? fmaxf(s0, 0.0f) : s0;
     }
   }
 }

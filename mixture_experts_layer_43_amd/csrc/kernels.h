@@ -12,6 +12,7 @@ struct RouteArgs {
   const float* w_router;   // [N_r, d]
   const float* bias;       // [N_r] or null
   int T, d, n_routed, top_k, gate;
+  bool bias_sel;           // bias enters the selection only (gates from the unbiased logits)
   bool x_bf16;
   int32_t* topk_idx;       // [T, K']
   float* topk_w;           // [T, K']
@@ -84,6 +85,7 @@ enum GemmMode { kGateUp = 0, kDown = 1 };
 // Bx0/Bx1 + s*bx_group_stride (bx_bytes per matrix), and with a gather its
 // row r reads A row (r - extra_base) % extra_rows (every token once).
 struct GemmArgs {
+  bool relu;               // kDown only: C[r, n] = max(A_r . B0_n, 0) (ReLU expert FFN)
   int64_t a_bytes;         // bytes of A readable through row indices (< 4 GB)
   int64_t b_bytes;         // bytes of one group's B0 (and of its B1) (< 4 GB)
   const int32_t* offsets;

@@ -61,15 +61,18 @@ struct StatAcc {
   }
 };
 
-// Top-K' of one token's logits z (lane-per-expert inside a group of NP
-// lanes, EPL experts per lane: expert e[q] = lane-in-group + NP*q), gate
-// values, and the ascending-id store.  K' rounds of group arg-max, ties to
-// the lower id; softmax over all routed experts (gate 0) or over the chosen
-// ones (gate 1), both relative to the largest logit.  STATS: also adds the
-// token's full softmax s (both gates), its choices and lse^2 to sa, and
-// writes lse[t] when lse is set.
+// Top-K' of one token (lane-per-expert inside a group of NP lanes, EPL
+// experts per lane: expert e[q] = lane-in-group + NP*q), gate values, and
+// the ascending-id store.  K' rounds of group arg-max on the selection
+// logits z, ties to the lower id; gate values from the gate logits zg:
+// softmax over all routed experts (gate 0) or over the chosen ones (gate 1),
+// relative to the largest logit of that set.  zg is z itself unless the bias
+// is for selection only (bias_sel).  STATS: also adds the token's full
+// softmax of zg (both gates), its choices and lse(zg)^2 to sa, and writes
+// lse[t] when lse is set.
 template <int NP, int EPL, bool STATS = false>
-__device__ __forceinline__ void select_and_store(const float (&z)[EPL], const int (&e)[EPL],
+__device__ __forceinline__ void select_and_store(const float (&z)[EPL], const float (&zg)[EPL],
+                                                 bool bias_sel, const int (&e)[EPL],
                                                  const bool (&ev)[EPL], int64_t t, int K,
                                                  int gate, int grp, int lane,
                                                  int32_t* __restrict__ topk_idx,
@@ -96,11 +99,20 @@ __device__ __forceinline__ void select_and_store(const float (&z)[EPL], const in
     for (int q = 0; q < EPL; ++q)
       if (e[q] == cand) sel[q] = true;
   }
+  if (bias_sel) {
+    // Gates from the unbiased logits: the largest over all experts (gate 0)
+    // or over the chosen ones (gate 1).
+    float m = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < EPL; ++q)
+      if (gate == 0 || sel[q]) m = fmaxf(m, zg[q]);
+    zmax = group_max<NP>(m);
+  }
   float ex[EPL];
   float part = 0.0f;
 #pragma unroll
   for (int q = 0; q < EPL; ++q) {
-    ex[q] = ev[q] ? expf(z[q] - zmax) : 0.0f;
+    ex[q] = ev[q] ? expf(zg[q] - zmax) : 0.0f;
     if (gate == 0 || sel[q]) part += ex[q];
   }
   const float denom = group_sum<NP>(part);
@@ -118,19 +130,34 @@ __device__ __forceinline__ void select_and_store(const float (&z)[EPL], const in
     prior += __popcll(m);
   }
   if constexpr (STATS) {
+    // Full softmax of zg relative to its largest value.  ex already is,
+    // except for gate 1 with a selection-only bias (its zmax is the chosen
+    // set's).
+    float zall = zmax;
+    float exs[EPL];
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) exs[q] = ex[q];
+    if (bias_sel && gate != 0) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < EPL; ++q) m = fmaxf(m, zg[q]);
+      zall = group_max<NP>(m);
+#pragma unroll
+      for (int q = 0; q < EPL; ++q) exs[q] = ev[q] ? expf(zg[q] - zall) : 0.0f;
+    }
     float full = denom;
     if (gate != 0) {
       float pf = 0.0f;
 #pragma unroll
-      for (int q = 0; q < EPL; ++q) pf += ex[q];
+      for (int q = 0; q < EPL; ++q) pf += exs[q];
       full = group_sum<NP>(pf);
     }
 #pragma unroll
     for (int q = 0; q < EPL; ++q) {
-      sa->p[q] += static_cast<double>(ex[q] / full);
+      sa->p[q] += static_cast<double>(exs[q] / full);
       sa->c[q] += sel[q] ? 1 : 0;
     }
-    const double l = static_cast<double>(zmax) + log(static_cast<double>(full));
+    const double l = static_cast<double>(zall) + log(static_cast<double>(full));
     sa->z2 += l * l;
     if (lse != nullptr && (lane % NP) == 0) lse[t] = static_cast<float>(l);
   }
@@ -175,7 +202,7 @@ __device__ __forceinline__ void block_stats(StatAcc<EPL>& sa, int lane, int wave
 template <typename XT, int NP, int EPL, bool STATS>
 __global__ __launch_bounds__(kRouterThreads) void router_kernel(
     const XT* __restrict__ x, const float* __restrict__ wg, const float* __restrict__ bias,
-    int T, int d, int Nr, int K, int gate, int32_t* __restrict__ topk_idx,
+    int T, int d, int Nr, int K, int gate, bool bias_sel, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, double* __restrict__ stats_part, float* __restrict__ lse) {
   constexpr int G = kWave / NP;
   const int lane = threadIdx.x & (kWave - 1);
@@ -240,10 +267,14 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(
   for (int i = 0; i < kTPL; ++i) {
     const int64_t t = tok0 + i;
     if (t >= T) break;  // uniform within the group
-    float z[EPL];
+    float z[EPL], zg[EPL];
 #pragma unroll
-    for (int q = 0; q < EPL; ++q) z[q] = ev[q] ? acc[i][q] + bq[q] : -INFINITY;
-    select_and_store<NP, EPL, STATS>(z, e, ev, t, K, gate, grp, lane, topk_idx, topk_w, &sa, lse);
+    for (int q = 0; q < EPL; ++q) {
+      z[q] = ev[q] ? acc[i][q] + bq[q] : -INFINITY;
+      zg[q] = ev[q] ? (bias_sel ? acc[i][q] : acc[i][q] + bq[q]) : -INFINITY;
+    }
+    select_and_store<NP, EPL, STATS>(z, zg, bias_sel, e, ev, t, K, gate, grp, lane, topk_idx,
+                                     topk_w, &sa, lse);
   }
   if constexpr (STATS) {
     __shared__ double red[(kRouterThreads / kWave) * (2 * NP * EPL + 1)];
@@ -264,11 +295,11 @@ hipError_t launch_t(const RouteArgs& a, hipStream_t s, int* nblk) {
   if (a.stats_part != nullptr)
     hipLaunchKernelGGL((router_kernel<XT, NP, EPL, true>), dim3(grid), dim3(kRouterThreads), 0, s,
                        static_cast<const XT*>(a.x), a.w_router, a.bias, a.T, a.d, a.n_routed,
-                       a.top_k, a.gate, a.topk_idx, a.topk_w, a.stats_part, a.lse);
+                       a.top_k, a.gate, a.bias_sel, a.topk_idx, a.topk_w, a.stats_part, a.lse);
   else
     hipLaunchKernelGGL((router_kernel<XT, NP, EPL, false>), dim3(grid), dim3(kRouterThreads), 0, s,
                        static_cast<const XT*>(a.x), a.w_router, a.bias, a.T, a.d, a.n_routed,
-                       a.top_k, a.gate, a.topk_idx, a.topk_w, nullptr, nullptr);
+                       a.top_k, a.gate, a.bias_sel, a.topk_idx, a.topk_w, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -383,7 +414,7 @@ __device__ __forceinline__ void router_round(f32x16 (&acc)[MBLK][NBLK],
 template <int MBLK, int NBLK, bool STATS>
 __global__ __launch_bounds__(kRW * kWave) void router_mfma_kernel(
     const bf16_t* __restrict__ x, const float* __restrict__ wg, const float* __restrict__ bias,
-    int T, int d, int Nr, int K, int gate, int32_t* __restrict__ topk_idx,
+    int T, int d, int Nr, int K, int gate, bool bias_sel, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, int KS, float* __restrict__ partial,
     double* __restrict__ stats_part, float* __restrict__ lse) {
   constexpr int TB = 32 * MBLK;
@@ -483,10 +514,18 @@ __global__ __launch_bounds__(kRW * kWave) void router_mfma_kernel(
   for (int tl = wave * (TB / kRW) + grp; tl < (wave + 1) * (TB / kRW); tl += G) {
     const int64_t t = tok0 + tl;
     if (t >= T) break;  // uniform within the group
-    float z[EPL];
+    float z[EPL], zg[EPL];
 #pragma unroll
-    for (int q = 0; q < EPL; ++q) z[q] = evq[q] ? lg[tl][e[q]] + bq[q] : -INFINITY;
-    select_and_store<NP, EPL, STATS>(z, e, evq, t, K, gate, grp, lane, topk_idx, topk_w, &sa, lse);
+    for (int q = 0; q < EPL; ++q) {
+      // Read first, then select values (e[q] < NPAD, inside the tile): a
+      // select between two loads would become a load through a selected
+      // pointer and push z to scratch.
+      const float v = lg[tl][e[q]];
+      z[q] = evq[q] ? v + bq[q] : -INFINITY;
+      zg[q] = evq[q] ? (bias_sel ? v : v + bq[q]) : -INFINITY;
+    }
+    select_and_store<NP, EPL, STATS>(z, zg, bias_sel, e, evq, t, K, gate, grp, lane, topk_idx,
+                                     topk_w, &sa, lse);
   }
   if constexpr (STATS)
     block_stats<NP, EPL, kRW>(sa, lane, wave, reinterpret_cast<double*>(&lg[0][0]),
@@ -514,7 +553,7 @@ __device__ __forceinline__ float sum_partials(const float* __restrict__ partial,
 template <int NBLK>
 __global__ __launch_bounds__(kWave) void router_select_kernel(
     const float* __restrict__ partial, const float* __restrict__ bias, int T, int Nr, int K,
-    int gate, int KS, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+    int gate, bool bias_sel, int KS, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
   constexpr int NPAD = 32 * NBLK;
   constexpr int NP = 16;
   constexpr int EPL = NPAD / NP;
@@ -525,15 +564,17 @@ __global__ __launch_bounds__(kWave) void router_select_kernel(
   if (t >= T) return;  // uniform within the group
   int e[EPL];
   bool evq[EPL];
-  float z[EPL];
+  float z[EPL], zg[EPL];
 #pragma unroll
   for (int q = 0; q < EPL; ++q) {
     e[q] = gl + NP * q;
     evq[q] = e[q] < Nr;
-    z[q] = sum_partials<NPAD>(partial, KS, T, t, e[q]);
-    z[q] = evq[q] ? z[q] + (bias != nullptr ? bias[e[q]] : 0.0f) : -INFINITY;
+    const float v = sum_partials<NPAD>(partial, KS, T, t, e[q]);
+    const float b = bias != nullptr && evq[q] ? bias[e[q]] : 0.0f;
+    z[q] = evq[q] ? v + b : -INFINITY;
+    zg[q] = evq[q] ? (bias_sel ? v : v + b) : -INFINITY;
   }
-  select_and_store<NP, EPL>(z, e, evq, t, K, gate, grp, lane, topk_idx, topk_w);
+  select_and_store<NP, EPL>(z, zg, bias_sel, e, evq, t, K, gate, grp, lane, topk_idx, topk_w);
 }
 
 template <int MBLK, int NBLK>
@@ -544,7 +585,7 @@ hipError_t launch_mfma(const RouteArgs& a, hipStream_t s, int* nblk) {
   if (a.stats_part != nullptr) {
     hipLaunchKernelGGL((router_mfma_kernel<MBLK, NBLK, true>), dim3(blocks, 1), dim3(kRW * kWave), 0,
                        s, static_cast<const bf16_t*>(a.x), a.w_router, a.bias, a.T, a.d,
-                       a.n_routed, a.top_k, a.gate, a.topk_idx, a.topk_w, 1, nullptr,
+                       a.n_routed, a.top_k, a.gate, a.bias_sel, a.topk_idx, a.topk_w, 1, nullptr,
                        a.stats_part, a.lse);
     return hipGetLastError();
   }
@@ -552,12 +593,14 @@ hipError_t launch_mfma(const RouteArgs& a, hipStream_t s, int* nblk) {
   const int KS = (a.partial != nullptr && MBLK == 1) ? max(1, min(kRouterSplit, 128 / blocks)) : 1;
   hipLaunchKernelGGL((router_mfma_kernel<MBLK, NBLK, false>), dim3(blocks, KS), dim3(kRW * kWave), 0, s,
                      static_cast<const bf16_t*>(a.x), a.w_router, a.bias, a.T, a.d, a.n_routed,
-                     a.top_k, a.gate, a.topk_idx, a.topk_w, KS, a.partial, nullptr, nullptr);
+                     a.top_k, a.gate, a.bias_sel, a.topk_idx, a.topk_w, KS, a.partial, nullptr,
+                     nullptr);
   if (KS == 1) return hipGetLastError();
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((router_select_kernel<NBLK>), dim3((a.T + 3) / 4), dim3(kWave), 0, s,
-                     a.partial, a.bias, a.T, a.n_routed, a.top_k, a.gate, KS, a.topk_idx, a.topk_w);
+                     a.partial, a.bias, a.T, a.n_routed, a.top_k, a.gate, a.bias_sel, KS, a.topk_idx,
+                     a.topk_w);
   return hipGetLastError();
 }
 

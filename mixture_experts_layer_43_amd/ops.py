@@ -18,6 +18,8 @@ from ._lib import MoeLayer, call
 
 _DT = {"f32": (_lib.MOE_F32, torch.float32), "bf16": (_lib.MOE_BF16, torch.bfloat16)}
 _GATE = {"softmax_topk": _lib.MOE_GATE_SOFTMAX_TOPK, "topk_softmax": _lib.MOE_GATE_TOPK_SOFTMAX}
+_FFN = {"silu": _lib.MOE_FFN_SILU_GATED, "relu": _lib.MOE_FFN_RELU}
+_BIAS = {"logits": _lib.MOE_BIAS_LOGITS, "selection": _lib.MOE_BIAS_SELECTION}
 
 
 @dataclass(frozen=True)
@@ -34,12 +36,15 @@ class Layer:
     dtype: str = "bf16"
     capacity: int = 0       # slots per expert per token group; 0 = dropless
     group_size: int = 0     # tokens per capacity group; 0 = the whole batch
+    ffn: str = "silu"       # "silu" (W1, W3, W2) or "relu" (wi = w_gate, wo = w_down)
+    bias_mode: str = "logits"  # "logits": bias in selection and gates; "selection": selection only
 
     @classmethod
     def of(cls, cfg) -> "Layer":
         return cls(cfg.d_model, cfg.n_routed, cfg.n_shared, cfg.top_k, cfg.d_ff,
                    cfg.d_ff_shared, cfg.gate, cfg.dtype, getattr(cfg, "capacity", 0),
-                   getattr(cfg, "group_size", 0))
+                   getattr(cfg, "group_size", 0), getattr(cfg, "ffn", "silu"),
+                   getattr(cfg, "bias_mode", "logits"))
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -48,7 +53,7 @@ class Layer:
     def c(self) -> MoeLayer:
         return MoeLayer(self.d_model, self.n_routed, self.n_shared, self.top_k, self.d_ff,
                         self.d_ff_shared, _GATE[self.gate], _DT[self.dtype][0], self.capacity,
-                        self.group_size)
+                        self.group_size, _FFN[self.ffn], _BIAS[self.bias_mode])
 
 
 def _p(t):
