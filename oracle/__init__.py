@@ -20,6 +20,9 @@ from .moe import (  # noqa: F401
     gate_values,
     route,
     route_selection_bias,
+    noisy_logits,
+    selection_and_gate_logits,
+    softplus,
     router_logits,
     select_topk,
     shared_ffn,

@@ -14,7 +14,7 @@ import numpy as np
 
 from synth import redraw_x_rows
 
-from .moe import decode, router_logits
+from .moe import decode, selection_and_gate_logits
 
 
 def topk_gap(z: np.ndarray, k: int) -> np.ndarray:
@@ -27,10 +27,15 @@ def topk_gap(z: np.ndarray, k: int) -> np.ndarray:
 
 def enforce_gap(cfg, inputs: dict, max_attempts: int = 64) -> int:
     """Redraw x rows in place until every token meets the gap; returns #tokens redrawn."""
-    wr = np.asarray(inputs["w_router"], dtype=np.float64)
-    b = None if inputs.get("bias") is None else np.asarray(inputs["bias"], dtype=np.float64)
     x = inputs["x"]
-    z = router_logits(decode(x, cfg.dtype), wr, b)
+
+    def sel_logits(rows):
+        sub = dict(inputs)
+        if inputs.get("noise") is not None:
+            sub["noise"] = inputs["noise"][rows]
+        return selection_and_gate_logits(cfg, sub, decode(x[rows], cfg.dtype))[0]
+
+    z = sel_logits(np.arange(x.shape[0]))
     bad = np.nonzero(topk_gap(z, cfg.top_k) < cfg.gap)[0]
     redrawn = int(bad.size)
     attempt = 0
@@ -38,7 +43,7 @@ def enforce_gap(cfg, inputs: dict, max_attempts: int = 64) -> int:
         if attempt >= max_attempts:
             raise RuntimeError(f"gap rule not met for {bad.size} tokens after {max_attempts} redraws")
         x[bad] = redraw_x_rows(cfg, bad, attempt)
-        zb = router_logits(decode(x[bad], cfg.dtype), wr, b)
+        zb = sel_logits(bad)
         bad = bad[topk_gap(zb, cfg.top_k) < cfg.gap]
         attempt += 1
     return redrawn

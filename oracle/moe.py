@@ -26,6 +26,10 @@ Readings taken where the pages leave a step open:
     in ascending order.
   * shared experts enter with weight 1 (eq. 9, first sum); the residual
     u_t of eq. 9 is added only when asked for.
+  * noisy top-k gating ([P4] section 2) when the inputs carry w_noise and
+    noise: the standard normal draws are an input [T, N_r] (the method's
+    random numbers come from outside), the noise term is part of the logits
+    for both the selection and the gates, and the bias is added after it.
   * with cfg.bias_mode == "selection" the bias steers only the top-K'
     choice and the gates come from the unbiased logits (the article that
     describes the bias does not say whether it enters the gate value);
@@ -59,6 +63,38 @@ def router_logits(x: np.ndarray, w_router: np.ndarray, bias=None) -> np.ndarray:
     if bias is not None:
         z = z + bias[None, :]
     return z
+
+
+def softplus(v: np.ndarray) -> np.ndarray:
+    """log(1 + e^v), evaluated without overflow."""
+    return np.logaddexp(0.0, v)
+
+
+def noisy_logits(x: np.ndarray, w_router: np.ndarray, w_noise: np.ndarray, eps: np.ndarray) -> np.ndarray:
+    """Noisy top-k gating's H(x)_i = (x W_g)_i + StandardNormal() * Softplus((x W_noise)_i)
+    ([P4] section 2), with the standard normal draws given as eps [T, N_r]."""
+    return x @ w_router.T + eps * softplus(x @ w_noise.T)
+
+
+def selection_and_gate_logits(cfg, inputs: dict, x: np.ndarray):
+    """(logits the top-K' is taken on, logits the gate values come from) for
+    the rows x: the affinities (plus the noise term of noisy gating when the
+    inputs carry w_noise and noise), with the bias added to both, or to the
+    selection logits only when cfg.bias_mode == "selection"."""
+    wr = np.asarray(inputs["w_router"], dtype=np.float64)
+    b = None if inputs.get("bias") is None else np.asarray(inputs["bias"], dtype=np.float64)
+    if inputs.get("w_noise") is not None:
+        eps = np.asarray(inputs["noise"], dtype=np.float64)
+        if eps.shape[0] != x.shape[0]:
+            raise ValueError("noise rows must match x rows")
+        z = noisy_logits(x, wr, np.asarray(inputs["w_noise"], dtype=np.float64), eps)
+        zb = z if b is None else z + b[None, :]
+    else:
+        z = router_logits(x, wr)
+        zb = z if b is None else router_logits(x, wr, b)
+    if b is not None and getattr(cfg, "bias_mode", "logits") == "selection":
+        return zb, z
+    return zb, zb
 
 
 def softmax(z: np.ndarray) -> np.ndarray:
@@ -106,7 +142,12 @@ def route_selection_bias(z: np.ndarray, bias: np.ndarray, k: int, gate: str):
     steers the load, the balancing without an auxiliary loss of the Tencent
     Cloud "DeepSeek MoE" article), the gate values on the unbiased z.  z are
     the logits without the bias."""
-    idx, _ = route(z + bias[None, :], k, gate)
+    return route_on(z + bias[None, :], z, k, gate)
+
+
+def route_on(zs: np.ndarray, z: np.ndarray, k: int, gate: str):
+    """Top-K' chosen on the logits zs, gate values from the logits z."""
+    idx, _ = route(zs, k, gate)
     return idx, gate_values(z, idx, gate)
 
 
@@ -170,18 +211,12 @@ def forward(cfg, inputs: dict, tokens=None, residual: bool = False) -> dict:
     """
     dt = cfg.dtype
     x = decode(inputs["x"], dt)
-    wr = np.asarray(inputs["w_router"], dtype=np.float64)
-    b = None if inputs.get("bias") is None else np.asarray(inputs["bias"], dtype=np.float64)
     T, d = x.shape
     Nr, k = cfg.n_routed, cfg.top_k
     kind = getattr(cfg, "ffn", "silu")
 
-    if getattr(cfg, "bias_mode", "logits") == "selection" and b is not None:
-        z = router_logits(x, wr)
-        idx, g = route_selection_bias(z, b, k, cfg.gate)
-    else:
-        z = router_logits(x, wr, b)
-        idx, g = route(z, k, cfg.gate)
+    zs, z = selection_and_gate_logits(cfg, inputs, x)
+    idx, g = route(z, k, cfg.gate) if zs is z else route_on(zs, z, k, cfg.gate)
     cap = getattr(cfg, "capacity", 0)
     if cap > 0:
         # Expert capacity ([P4] section 3): dropped assignments get gate 0.

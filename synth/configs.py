@@ -35,6 +35,7 @@ class LayerConfig:
     dtype: str = "bf16"        # storage/compute type of x, expert weights, y
     zipf_s: float = 0.0        # > 0: per-expert router bias -s*ln(e+1)
     bias_mode: str = "logits"  # "logits": bias in selection and gates; "selection": selection only
+    noisy: bool = False        # noisy top-k gating: inputs gain w_noise [N_r, d] and noise [T, N_r]
     seed: int = 4300
     gap: float = 1e-3          # min logit gap between the K'-th and (K'+1)-th
     ffn: str = "silu"          # "silu": W2 (silu(W1 u) * (W3 u)); "relu": wo ReLU(wi u) (W1, W2)

@@ -5,6 +5,8 @@ Recipe (every draw is float32 standard normal from numpy's PCG64):
                               block b from stream (seed, 0, b)
   w_router    [N_r, d] f32    N(0, 1/d)                 stream (seed, 1)
   bias        [N_r]    f32    -s * ln(e + 1) for Zipf(s) skew, else absent
+  w_noise     [N_r, d] f32    N(0, 1/d), noisy gating only   stream (seed, 10)
+  noise       [T, N_r] f32    N(0, 1), the gating noise draws  stream (seed, 11)
   w_gate      [N_r, I, d]     N(0, 1/d)   expert e from stream (seed, 2, e)
   w_up        [N_r, I, d]     N(0, 1/d)                  stream (seed, 3, e)
   w_down      [N_r, d, I]     N(0, 1/I)                  stream (seed, 4, e)
@@ -114,6 +116,11 @@ def make_inputs(cfg: LayerConfig, seed: int | None = None, experts: bool = True)
         out["x"] = make_x(cfg, seed, pool)
         out["w_router"] = _normal((Nr, d), 1.0 / np.sqrt(d), seed, 1)
         out["bias"] = zipf_bias(Nr, cfg.zipf_s) if cfg.zipf_s > 0 else None
+        if cfg.noisy:
+            # Noisy top-k gating: W_noise like W_g, and the standard normal
+            # draws of every (token, expert), an input of the method.
+            out["w_noise"] = _normal((Nr, d), 1.0 / np.sqrt(d), seed, 10)
+            out["noise"] = _normal((T, Nr), 1.0, seed, 11)
         if experts:
             for name, tensor, shape, std in (
                 ("w_gate", 2, (Nr, I, d), 1.0 / np.sqrt(d)),

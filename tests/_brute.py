@@ -57,13 +57,16 @@ def _gates(z, k, gate):
 
 def brute_forward(x, w_router, bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
                   top_k, gate, residual=False, capacity=0, group_size=0, ffn="silu",
-                  bias_mode="logits"):
+                  bias_mode="logits", w_noise=None, noise=None):
     """All arguments are nested Python lists of floats (bias may be None).
 
     capacity > 0: each expert takes at most `capacity` tokens per group of
     `group_size` consecutive tokens (0: the whole batch), first come first
     served in token order; a token that finds a chosen expert full loses that
     expert's gate (MoE-survey blog page, section 3, expert capacity).
+
+    w_noise, noise: noisy top-k gating (MoE-survey blog page, section 2): the
+    logit of expert i becomes u . w_i + noise[t][i] * log(1 + exp(u . wn_i)).
 
     bias_mode "selection": the bias takes part in choosing the experts only;
     the gate values come from the logits without it.
@@ -80,10 +83,14 @@ def brute_forward(x, w_router, bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_do
     S = group_size if 0 < group_size < len(x) else len(x)
     taken = {}
     for t, u in enumerate(x):
-        z = [_dot(w_router[i], u) + (bias[i] if bias is not None else 0.0) for i in range(n)]
+        base = [_dot(w_router[i], u) for i in range(n)]
+        if w_noise is not None:
+            base = [base[i] + noise[t][i] * math.log1p(math.exp(_dot(w_noise[i], u)))
+                    for i in range(n)]
+        z = [base[i] + (bias[i] if bias is not None else 0.0) for i in range(n)]
         chosen, g = _gates(z, top_k, gate)
         if bias_mode == "selection" and bias is not None:
-            z0 = [_dot(w_router[i], u) for i in range(n)]
+            z0 = base
             _, g0 = _gates(z0, n, gate)            # gates of every expert, unbiased
             if gate == "topk_softmax":
                 m = max(z0[i] for i in chosen)

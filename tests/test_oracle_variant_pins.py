@@ -164,3 +164,72 @@ def test_planted_selection_mistake_is_caught(name, monkeypatch):
         except AssertionError:
             failed += 1
     assert failed > 0, f"planted mistake {name!r} passed every pin"
+
+
+# --- noisy top-k gating -----------------------------------------------------
+NOISY_CASES = [dict(ffn="silu", noisy=True, gate="topk_softmax"),
+               dict(ffn="silu", noisy=True),
+               dict(ffn="relu", noisy=True, zipf_s=1.2, bias_mode="selection", gate="topk_softmax")]
+
+
+@pytest.mark.parametrize("kw", NOISY_CASES, ids=[str(c) for c in NOISY_CASES])
+def test_noisy_gating_matches_dense_brute_force(kw):
+    cfg = cfg_of(**kw)
+    inp = inputs(cfg)
+    L = {k: (None if v is None else np.asarray(v, np.float64).tolist()) for k, v in inp.items()}
+    chosen, g, y = brute_forward(L["x"], L["w_router"], L["bias"], L["w_gate"], L.get("w_up"),
+                                 L["w_down"], L["ws_gate"], L.get("ws_up"), L["ws_down"], cfg.top_k,
+                                 cfg.gate, False, ffn=cfg.ffn, bias_mode=cfg.bias_mode,
+                                 w_noise=L["w_noise"], noise=L["noise"])
+    r = om.forward(cfg, inp)
+    np.testing.assert_array_equal(r["topk_idx"], np.array(chosen))
+    np.testing.assert_allclose(r["y"], np.array(y), rtol=1e-12, atol=1e-12)
+
+
+def test_softplus_closed_forms():
+    np.testing.assert_allclose(om.softplus(np.array([0.0])), [np.log(2.0)], rtol=1e-15)
+    np.testing.assert_allclose(om.softplus(np.array([50.0, 800.0])), [50.0, 800.0], rtol=1e-15)
+    np.testing.assert_allclose(om.softplus(np.array([-40.0])), [np.exp(-40.0)], rtol=1e-12)
+    v = np.linspace(-5, 5, 11)
+    np.testing.assert_allclose(om.softplus(v) - om.softplus(-v), v, atol=1e-14)   # sp(v) - sp(-v) = v
+
+
+def test_noise_term_closed_form():
+    # W_noise = 0 makes every Softplus ln 2, so H = x W_g + eps ln 2; eps = 0
+    # gives the noiseless logits.
+    rng = np.random.default_rng(9)
+    x, wg, eps = rng.normal(size=(6, 5)), rng.normal(size=(4, 5)), rng.normal(size=(6, 4))
+    np.testing.assert_allclose(om.noisy_logits(x, wg, np.zeros((4, 5)), eps), x @ wg.T + eps * np.log(2.0),
+                               rtol=1e-14, atol=1e-14)
+    np.testing.assert_array_equal(om.noisy_logits(x, wg, rng.normal(size=(4, 5)), np.zeros((6, 4))), x @ wg.T)
+
+
+def test_zero_noise_is_the_noiseless_layer():
+    cfg = cfg_of(ffn="silu", noisy=True)
+    inp = inputs(cfg)
+    inp["noise"] = np.zeros_like(inp["noise"])
+    a = om.forward(cfg, inp)
+    b = om.forward(cfg.with_(noisy=False), {k: v for k, v in inp.items() if k not in ("w_noise", "noise")})
+    np.testing.assert_array_equal(a["topk_idx"], b["topk_idx"])
+    np.testing.assert_allclose(a["y"], b["y"], rtol=1e-15, atol=0)
+
+
+NOISE_MISTAKES = {
+    "noise without softplus": lambda x, wg, wn, eps: x @ wg.T + eps * (x @ wn.T),
+    "exp instead of softplus": lambda x, wg, wn, eps: x @ wg.T + eps * np.exp(x @ wn.T),
+    "noise scaled by the clean logit": lambda x, wg, wn, eps: x @ wg.T + eps * om.softplus(x @ wg.T),
+}
+NOISE_PINS = [lambda: [test_noisy_gating_matches_dense_brute_force(c) for c in NOISY_CASES],
+              test_noise_term_closed_form]
+
+
+@pytest.mark.parametrize("name", sorted(NOISE_MISTAKES))
+def test_planted_noise_mistake_is_caught(name, monkeypatch):
+    monkeypatch.setattr(om, "noisy_logits", NOISE_MISTAKES[name])
+    failed = 0
+    for pin in NOISE_PINS:
+        try:
+            pin()
+        except AssertionError:
+            failed += 1
+    assert failed > 0, f"planted mistake {name!r} passed every pin"
