@@ -19,6 +19,7 @@ from .moe import (  # noqa: F401
     forward,
     gate_values,
     route,
+    route_on,
     route_selection_bias,
     noisy_logits,
     selection_and_gate_logits,
