@@ -79,12 +79,18 @@ __device__ __forceinline__ void wait_steps(int ahead) {
   wait_vmcnt<0>();
 }
 
-// Workgroup barrier with no memory fence: the copies into LDS are waited for
-// explicitly (wait_steps) so that the ones for later K steps stay in flight.
-// The empty asm keeps the compiler from moving LDS accesses across it.
+// Workgroup barrier with no global memory fence: the copies into LDS are
+// waited for explicitly (wait_steps) so that the ones for later K steps stay
+// in flight.  This wavefront's own LDS reads must have returned, though: the
+// last K slice of a step is read just before the barrier and multiplied
+// after it, and right after the barrier other wavefronts start copying the
+// step after next into that same stage.  The empty asm keeps the compiler
+// from moving LDS accesses across the barrier.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::: "memory");
+  // lgkmcnt(0); vmcnt and expcnt at their maxima (not waited for).
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);

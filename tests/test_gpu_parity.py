@@ -273,6 +273,29 @@ def test_repeat_calls_are_deterministic():
     np.testing.assert_array_equal(a, b)
 
 
+@pytest.mark.parametrize("kw", [{}, dict(capacity=12)], ids=["dropless", "capacity"])
+def test_small_tiles_are_deterministic(kw):
+    """The decode shape runs 32-row tiles whose A rows often sit in the vector
+    L1, so an LDS copy can land quickly; the K loop must not let it overwrite
+    a stage another wavefront is still reading.  Fifty calls, identical bits."""
+    cfg = cfg_of("16b-decode").with_(**kw)
+    announce(f"determinism of small tiles {kw}")
+    inp = prepare(cfg)
+    d = upload(inp)
+    lay = ops.Layer.of(cfg)
+    f = ops.Forward(lay, cfg.tokens, torch.device("cuda"))
+    args = [d[k] for k in ("x", "w_router", "bias", "w_gate", "w_up", "w_down", "ws_gate", "ws_up",
+                           "ws_down")]
+    f(*args)
+    y0 = f.y.clone()
+    for _ in range(50):
+        f(*args, checked=True)
+    torch.cuda.synchronize()
+    for _ in range(50):
+        f(*args, checked=True)
+        assert torch.equal(f.y, y0)
+
+
 def test_forward_timed_matches_forward():
     """moe_forward_timed with only some markers set computes exactly what
     moe_forward computes, and every set marker pair brackets a stage."""
