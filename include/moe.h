@@ -142,6 +142,18 @@ int moe_workspace_size(const moe_layer* layer, int64_t T, size_t* bytes);
 int moe_route(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
               const float* logit_bias, int32_t* topk_idx, float* topk_w, void* stream);
 
+/* moe_route with noisy top-k gating (MoE-survey blog page, section 2):
+ *   H_t,i = (x_t W_g^T)_i + noise[t, i] * Softplus((x_t W_noise^T)_i)
+ * takes the place of the logits for both the selection and the gate values
+ * (logit_bias is added to H as layer->bias_mode says).  The method's random
+ * numbers are an input: noise [T, N_r] fp32 holds the caller's standard
+ * normal draws; w_noise [N_r, d] fp32.  Softplus(v) = log(1 + e^v).  The
+ * rest of the layer is the staged path: moe_permute, moe_expert_ffn,
+ * moe_shared_ffn, moe_combine. */
+int moe_route_noisy(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
+                    const float* logit_bias, const float* w_noise, const float* noise,
+                    int32_t* topk_idx, float* topk_w, void* stream);
+
 /* Floats written to `stats` by moe_route_stats for N_r experts, D groups. */
 #define MOE_STATS_LEN(n_routed, n_devices) (2 * (n_routed) + 2 * (n_devices) + 3)
 

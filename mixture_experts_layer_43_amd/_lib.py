@@ -15,7 +15,7 @@ MOE_BIAS_LOGITS, MOE_BIAS_SELECTION = 0, 1
 
 EXPORTS = (
     "moe_abi_version", "moe_status_str", "moe_last_hip_error", "moe_workspace_size",
-    "moe_route", "moe_route_stats", "moe_permute", "moe_expert_ffn", "moe_shared_ffn", "moe_combine",
+    "moe_route", "moe_route_noisy", "moe_route_stats", "moe_permute", "moe_expert_ffn", "moe_shared_ffn", "moe_combine",
     "moe_forward", "moe_forward_timed",
 )
 MOE_NUM_STAGES = 7
@@ -50,6 +50,7 @@ _SIGS = {
     "moe_last_hip_error": ([], ctypes.c_int),
     "moe_workspace_size": ([LP, I64, ctypes.POINTER(SZ)], ctypes.c_int),
     "moe_route": ([LP, I64, P, P, P, P, P, P], ctypes.c_int),
+    "moe_route_noisy": ([LP, I64, P, P, P, P, P, P, P, P], ctypes.c_int),
     "moe_route_stats": ([LP, I64, P, P, P, ctypes.c_int32, P, P, P, P, P, SZ, P], ctypes.c_int),
     "moe_permute": ([LP, I64, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
     "moe_expert_ffn": ([LP, I64, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),

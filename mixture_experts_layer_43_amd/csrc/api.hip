@@ -358,6 +358,25 @@ int moe_route(const moe_layer* layer, int64_t T, const void* x, const float* w_r
   return route_impl(layer, T, x, w_router, logit_bias, topk_idx, topk_w, nullptr, stream);
 }
 
+int moe_route_noisy(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
+                    const float* logit_bias, const float* w_noise, const float* noise,
+                    int32_t* topk_idx, float* topk_w, void* stream) {
+  MOE_TRY(check_layer(layer, T));
+  MOE_TRY(needT(x, T));
+  MOE_TRY(need(w_router));
+  MOE_TRY(opt(logit_bias));
+  MOE_TRY(need(w_noise));
+  MOE_TRY(needT(noise, T));
+  MOE_TRY(needT(topk_idx, T));
+  MOE_TRY(needT(topk_w, T));
+  if (T == 0) return MOE_OK;
+  moe::RouteArgs a = route_args(layer, T, x, w_router, logit_bias, topk_idx, topk_w, nullptr);
+  a.w_noise = w_noise;
+  a.noise = noise;
+  MOE_HIP(moe::launch_route(a, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
 int moe_route_stats(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
                     const float* logit_bias, int32_t n_devices, int32_t* topk_idx, float* topk_w,
                     float* stats, float* lse, void* ws, size_t ws_bytes, void* stream) {

@@ -19,6 +19,8 @@ struct RouteArgs {
   float* partial;          // null, or scratch of router_partial_bytes(T) for split-K logits
   double* stats_part;      // null, or scratch of route_stats_bytes(T): routing statistics on
   float* lse;              // [T] or null: per-token log-sum-exp (statistics only)
+  const float* w_noise;    // [N_r, d] or null: noisy top-k gating (no split, no statistics)
+  const float* noise;      // [T, N_r] standard normal draws, with w_noise
 };
 // Split-K of the matrix-core router for small batches: at most this many
 // K slices, each writing a [T, 128] fp32 partial tile.

@@ -45,6 +45,10 @@ __device__ __forceinline__ void load4<bf16_t>(const bf16_t* p, float (&v)[4]) {
   v[3] = __uint_as_float(q.y & 0xFFFF0000u);
 }
 
+// log(1 + e^v) in fp32: the noise scale of noisy top-k gating.  Above 20
+// the correction log1p(e^-v) is below fp32 resolution.
+__device__ __forceinline__ float softplus_f32(float v) { return v > 20.0f ? v : log1pf(expf(v)); }
+
 // Running sums of the routing statistics (DeepSeekMoE page, section 3.3,
 // eq. 13-14; MoE-survey blog page, section 5, z-loss) over the tokens one
 // lane's group has selected for: s_i and times chosen for each expert the
@@ -199,11 +203,15 @@ __device__ __forceinline__ void block_stats(StatAcc<EPL>& sa, int lane, int wave
   }
 }
 
-template <typename XT, int NP, int EPL, bool STATS>
+// NOISE: noisy top-k gating (MoE-survey blog page, section 2): the logit of
+// expert i is x.w_i + eps[t][i] * softplus(x.wn_i), with a second fp32 dot
+// product per (token, expert) against W_noise.
+template <typename XT, int NP, int EPL, bool STATS, bool NOISE>
 __global__ __launch_bounds__(kRouterThreads) void router_kernel(
     const XT* __restrict__ x, const float* __restrict__ wg, const float* __restrict__ bias,
     int T, int d, int Nr, int K, int gate, bool bias_sel, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w, double* __restrict__ stats_part, float* __restrict__ lse) {
+    float* __restrict__ topk_w, double* __restrict__ stats_part, float* __restrict__ lse,
+    const float* __restrict__ wn, const float* __restrict__ eps) {
   constexpr int G = kWave / NP;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -219,11 +227,13 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(
   int e[EPL];
   bool ev[EPL];
   const float* wrow[EPL];
+  const float* nrow[EPL];
 #pragma unroll
   for (int q = 0; q < EPL; ++q) {
     e[q] = gl + NP * q;
     ev[q] = e[q] < Nr;
     wrow[q] = wg + static_cast<int64_t>(ev[q] ? e[q] : Nr - 1) * d;
+    nrow[q] = NOISE ? wn + static_cast<int64_t>(ev[q] ? e[q] : Nr - 1) * d : nullptr;
   }
   const XT* xrow[kTPL];
 #pragma unroll
@@ -233,15 +243,23 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(
   }
 
   float acc[kTPL][EPL];
+  float accn[NOISE ? kTPL : 1][EPL];
 #pragma unroll
   for (int i = 0; i < kTPL; ++i)
 #pragma unroll
-    for (int q = 0; q < EPL; ++q) acc[i][q] = 0.0f;
+    for (int q = 0; q < EPL; ++q) {
+      acc[i][q] = 0.0f;
+      if constexpr (NOISE) accn[i][q] = 0.0f;
+    }
 
   for (int k = 0; k < d; k += 4) {
     float w[EPL][4];
+    float wv[NOISE ? EPL : 1][4];
 #pragma unroll
-    for (int q = 0; q < EPL; ++q) load4<float>(wrow[q] + k, w[q]);
+    for (int q = 0; q < EPL; ++q) {
+      load4<float>(wrow[q] + k, w[q]);
+      if constexpr (NOISE) load4<float>(nrow[q] + k, wv[q]);
+    }
 #pragma unroll
     for (int i = 0; i < kTPL; ++i) {
       float xv[4];
@@ -254,6 +272,14 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(
         a = fmaf(xv[2], w[q][2], a);
         a = fmaf(xv[3], w[q][3], a);
         acc[i][q] = a;
+        if constexpr (NOISE) {
+          float b = accn[i][q];
+          b = fmaf(xv[0], wv[q][0], b);
+          b = fmaf(xv[1], wv[q][1], b);
+          b = fmaf(xv[2], wv[q][2], b);
+          b = fmaf(xv[3], wv[q][3], b);
+          accn[i][q] = b;
+        }
       }
     }
   }
@@ -270,8 +296,11 @@ __global__ __launch_bounds__(kRouterThreads) void router_kernel(
     float z[EPL], zg[EPL];
 #pragma unroll
     for (int q = 0; q < EPL; ++q) {
-      z[q] = ev[q] ? acc[i][q] + bq[q] : -INFINITY;
-      zg[q] = ev[q] ? (bias_sel ? acc[i][q] : acc[i][q] + bq[q]) : -INFINITY;
+      float h = acc[i][q];
+      if constexpr (NOISE)
+        h = fmaf(eps[t * Nr + (ev[q] ? e[q] : Nr - 1)], softplus_f32(accn[i][q]), h);
+      z[q] = ev[q] ? h + bq[q] : -INFINITY;
+      zg[q] = ev[q] ? (bias_sel ? h : h + bq[q]) : -INFINITY;
     }
     select_and_store<NP, EPL, STATS>(z, zg, bias_sel, e, ev, t, K, gate, grp, lane, topk_idx,
                                      topk_w, &sa, lse);
@@ -292,14 +321,21 @@ hipError_t launch_t(const RouteArgs& a, hipStream_t s, int* nblk) {
   static_assert(tok_per_block >= 32, "route_stats_bytes assumes >= 32 tokens per workgroup");
   const int grid = (a.T + tok_per_block - 1) / tok_per_block;
   *nblk = grid;
-  if (a.stats_part != nullptr)
-    hipLaunchKernelGGL((router_kernel<XT, NP, EPL, true>), dim3(grid), dim3(kRouterThreads), 0, s,
-                       static_cast<const XT*>(a.x), a.w_router, a.bias, a.T, a.d, a.n_routed,
-                       a.top_k, a.gate, a.bias_sel, a.topk_idx, a.topk_w, a.stats_part, a.lse);
+  if (a.w_noise != nullptr)
+    hipLaunchKernelGGL((router_kernel<XT, NP, EPL, false, true>), dim3(grid), dim3(kRouterThreads), 0,
+                       s, static_cast<const XT*>(a.x), a.w_router, a.bias, a.T, a.d, a.n_routed,
+                       a.top_k, a.gate, a.bias_sel, a.topk_idx, a.topk_w, nullptr, nullptr,
+                       a.w_noise, a.noise);
+  else if (a.stats_part != nullptr)
+    hipLaunchKernelGGL((router_kernel<XT, NP, EPL, true, false>), dim3(grid), dim3(kRouterThreads), 0,
+                       s, static_cast<const XT*>(a.x), a.w_router, a.bias, a.T, a.d, a.n_routed,
+                       a.top_k, a.gate, a.bias_sel, a.topk_idx, a.topk_w, a.stats_part, a.lse,
+                       nullptr, nullptr);
   else
-    hipLaunchKernelGGL((router_kernel<XT, NP, EPL, false>), dim3(grid), dim3(kRouterThreads), 0, s,
-                       static_cast<const XT*>(a.x), a.w_router, a.bias, a.T, a.d, a.n_routed,
-                       a.top_k, a.gate, a.bias_sel, a.topk_idx, a.topk_w, nullptr, nullptr);
+    hipLaunchKernelGGL((router_kernel<XT, NP, EPL, false, false>), dim3(grid), dim3(kRouterThreads), 0,
+                       s, static_cast<const XT*>(a.x), a.w_router, a.bias, a.T, a.d, a.n_routed,
+                       a.top_k, a.gate, a.bias_sel, a.topk_idx, a.topk_w, nullptr, nullptr,
+                       nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -416,7 +452,8 @@ __global__ __launch_bounds__(kRW * kWave) void router_mfma_kernel(
     const bf16_t* __restrict__ x, const float* __restrict__ wg, const float* __restrict__ bias,
     int T, int d, int Nr, int K, int gate, bool bias_sel, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, int KS, float* __restrict__ partial,
-    double* __restrict__ stats_part, float* __restrict__ lse) {
+    double* __restrict__ stats_part, float* __restrict__ lse, const float* __restrict__ wn,
+    const float* __restrict__ eps) {
   constexpr int TB = 32 * MBLK;
   constexpr int NPAD = 32 * NBLK;
   // Selection: groups of 16 lanes, one token each (4-step reductions).
@@ -442,13 +479,16 @@ __global__ __launch_bounds__(kRW * kWave) void router_mfma_kernel(
     const int64_t t = tok0 + mb * 32 + lr;
     xp[mb] = x + (t < T ? t : static_cast<int64_t>(T) - 1) * d + kh;
   }
+  // Rows of the logit tile: the N_r experts of W_g, then, for noisy gating
+  // (wn set), the N_r rows of W_noise (2 N_r <= 32*NBLK).
+  const int NE = wn != nullptr ? 2 * Nr : Nr;
   const float* wp[NBLK];
   bool ev[NBLK];
 #pragma unroll
   for (int nb = 0; nb < NBLK; ++nb) {
-    const int e = nb * 32 + lr;
-    ev[nb] = e < Nr;
-    wp[nb] = wg + static_cast<int64_t>(min(e, Nr - 1)) * d + kh;
+    const int e = min(nb * 32 + lr, NE - 1);
+    ev[nb] = nb * 32 + lr < NE;
+    wp[nb] = (e < Nr ? wg + static_cast<int64_t>(e) * d : wn + static_cast<int64_t>(e - Nr) * d) + kh;
   }
 
   f32x16 acc[MBLK][NBLK];
@@ -520,7 +560,11 @@ __global__ __launch_bounds__(kRW * kWave) void router_mfma_kernel(
       // Read first, then select values (e[q] < NPAD, inside the tile): a
       // select between two loads would become a load through a selected
       // pointer and push z to scratch.
-      const float v = lg[tl][e[q]];
+      float v = lg[tl][e[q]];
+      if (wn != nullptr) {   // noisy gating: + eps * softplus(x . wn_e), row N_r + e
+        const float nv = lg[tl][min(Nr + e[q], NPAD - 1)];
+        v = fmaf(eps[t * Nr + min(e[q], Nr - 1)], softplus_f32(nv), v);
+      }
       z[q] = evq[q] ? v + bq[q] : -INFINITY;
       zg[q] = evq[q] ? (bias_sel ? v : v + bq[q]) : -INFINITY;
     }
@@ -586,7 +630,14 @@ hipError_t launch_mfma(const RouteArgs& a, hipStream_t s, int* nblk) {
     hipLaunchKernelGGL((router_mfma_kernel<MBLK, NBLK, true>), dim3(blocks, 1), dim3(kRW * kWave), 0,
                        s, static_cast<const bf16_t*>(a.x), a.w_router, a.bias, a.T, a.d,
                        a.n_routed, a.top_k, a.gate, a.bias_sel, a.topk_idx, a.topk_w, 1, nullptr,
-                       a.stats_part, a.lse);
+                       a.stats_part, a.lse, nullptr, nullptr);
+    return hipGetLastError();
+  }
+  if (a.w_noise != nullptr) {
+    hipLaunchKernelGGL((router_mfma_kernel<MBLK, NBLK, false>), dim3(blocks, 1), dim3(kRW * kWave), 0,
+                       s, static_cast<const bf16_t*>(a.x), a.w_router, a.bias, a.T, a.d,
+                       a.n_routed, a.top_k, a.gate, a.bias_sel, a.topk_idx, a.topk_w, 1, nullptr,
+                       nullptr, nullptr, a.w_noise, a.noise);
     return hipGetLastError();
   }
   // Split K when the token blocks alone would leave most CUs idle.
@@ -594,7 +645,7 @@ hipError_t launch_mfma(const RouteArgs& a, hipStream_t s, int* nblk) {
   hipLaunchKernelGGL((router_mfma_kernel<MBLK, NBLK, false>), dim3(blocks, KS), dim3(kRW * kWave), 0, s,
                      static_cast<const bf16_t*>(a.x), a.w_router, a.bias, a.T, a.d, a.n_routed,
                      a.top_k, a.gate, a.bias_sel, a.topk_idx, a.topk_w, KS, a.partial, nullptr,
-                     nullptr);
+                     nullptr, nullptr, nullptr);
   if (KS == 1) return hipGetLastError();
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -618,11 +669,12 @@ hipError_t launch_x(const RouteArgs& a, hipStream_t s, int* nblk) {
 hipError_t launch_router(const RouteArgs& a, hipStream_t s, int* nblk) {
   if (a.x_bf16 && a.d % 64 == 0) {
     // Two token blocks per wavefront once there are enough tokens to fill
-    // the chip with 64-token workgroups.
+    // the chip with 64-token workgroups.  Noisy gating needs 2 N_r rows.
     const bool wide = a.T >= 64 * 256;
-    if (a.n_routed <= 32) return wide ? launch_mfma<2, 1>(a, s, nblk) : launch_mfma<1, 1>(a, s, nblk);
-    if (a.n_routed <= 64) return wide ? launch_mfma<2, 2>(a, s, nblk) : launch_mfma<1, 2>(a, s, nblk);
-    if (a.n_routed <= 128) return launch_mfma<1, 4>(a, s, nblk);
+    const int rows = a.w_noise != nullptr ? 2 * a.n_routed : a.n_routed;
+    if (rows <= 32) return wide ? launch_mfma<2, 1>(a, s, nblk) : launch_mfma<1, 1>(a, s, nblk);
+    if (rows <= 64) return wide ? launch_mfma<2, 2>(a, s, nblk) : launch_mfma<1, 2>(a, s, nblk);
+    if (rows <= 128) return launch_mfma<1, 4>(a, s, nblk);
   }
   return a.x_bf16 ? launch_x<bf16_t>(a, s, nblk) : launch_x<float>(a, s, nblk);
 }

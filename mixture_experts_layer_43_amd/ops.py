@@ -102,6 +102,22 @@ def route(layer: Layer, x, w_router, bias=None):
     return idx, w
 
 
+def route_noisy(layer: Layer, x, w_router, bias, w_noise, noise):
+    """Noisy top-k gating: the logits gain noise * softplus(x w_noise^T)."""
+    T = x.shape[0]
+    dt = layer.torch_dtype
+    _check(x, (T, layer.d_model), dt, "x")
+    _check(w_router, (layer.n_routed, layer.d_model), torch.float32, "w_router", x.device)
+    _check(bias, (layer.n_routed,), torch.float32, "bias", x.device)
+    _check(w_noise, (layer.n_routed, layer.d_model), torch.float32, "w_noise", x.device)
+    _check(noise, (T, layer.n_routed), torch.float32, "noise", x.device)
+    idx = torch.empty((T, layer.top_k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, layer.top_k), dtype=torch.float32, device=x.device)
+    call("moe_route_noisy", ctypes.byref(layer.c()), T, _p(x), _p(w_router), _p(bias), _p(w_noise),
+         _p(noise), _p(idx), _p(w), _stream())
+    return idx, w
+
+
 def stats_len(layer: Layer, n_devices: int) -> int:
     return 2 * layer.n_routed + 2 * n_devices + 3
 

@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     L = _lib.lib()
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib.EXPORTS)

@@ -69,6 +69,7 @@ def test_forward_with_capacity_matches_oracle(name, factor, S):
     inp = prepare(cfg)
     ref = oracle.forward(cfg, inp)
     f = run_forward(cfg, upload(inp))
+    np.testing.assert_array_equal(host(f.topk_idx), ref["topk_idx"])
     np.testing.assert_array_equal(host(f.counts), ref["counts"])
     np.testing.assert_array_equal(host(f.offsets), ref["offsets"])
     check_y(host(f.y), ref["y"], cfg.dtype)

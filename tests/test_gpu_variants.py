@@ -126,3 +126,66 @@ def test_selection_bias_changes_gates_only_where_bias_is_set():
     b = ops.route(ops.Layer.of(cfg.with_(bias_mode="selection")), d["x"], d["w_router"], None)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ---- noisy top-k gating --------------------------------------------------------
+NOISY = ["mid-gshard", "mid-ragged", "16b-decode", "2b", "mid-f32", "mid-many-experts", "mid-wide-k"]
+
+
+def noisy_ref(cfg, inp):
+    x = oracle.decode(inp["x"], cfg.dtype)
+    zs, z = oracle.selection_and_gate_logits(cfg, inp, x)
+    return oracle.route_on(zs, z, cfg.top_k, cfg.gate)
+
+
+@pytest.mark.parametrize("name", NOISY)
+def test_noisy_route_matches_oracle(name):
+    cfg = cfg_of(name).with_(noisy=True)
+    announce(f"noisy route {name}")
+    inp = prepare(cfg)
+    idx, g = noisy_ref(cfg, inp)
+    d = upload(inp)
+    gi, gw = ops.route_noisy(ops.Layer.of(cfg), d["x"], d["w_router"], d["bias"], d["w_noise"],
+                             d["noise"])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(gi), idx)
+    check_gates(host(gw), g)
+
+
+def test_noisy_route_with_selection_bias_and_zero_noise():
+    cfg = MID["mid-gshard"].with_(noisy=True, bias_mode="selection", zipf_s=1.5)
+    announce("noisy route, selection-only bias; zero noise = moe_route")
+    inp = prepare(cfg)
+    idx, g = noisy_ref(cfg, inp)
+    d = upload(inp)
+    lay = ops.Layer.of(cfg)
+    gi, gw = ops.route_noisy(lay, d["x"], d["w_router"], d["bias"], d["w_noise"], d["noise"])
+    zi, zw = ops.route_noisy(lay, d["x"], d["w_router"], d["bias"], d["w_noise"],
+                             torch.zeros_like(d["noise"]))
+    ri, rw = ops.route(lay, d["x"], d["w_router"], d["bias"])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(gi), idx)
+    check_gates(host(gw), g)
+    assert torch.equal(zi, ri)
+    np.testing.assert_allclose(host(zw), host(rw), rtol=1e-6)
+
+
+@pytest.mark.parametrize("name", ["mid-ragged", "mid-gshard"])
+def test_noisy_layer_through_the_staged_calls(name):
+    """route_noisy -> permute -> expert_ffn -> shared_ffn -> combine gives the
+    oracle's noisy-gated layer."""
+    cfg = cfg_of(name).with_(noisy=True)
+    announce(f"noisy layer, staged {name}")
+    inp = prepare(cfg)
+    ref = oracle.forward(cfg, inp)
+    d = upload(inp)
+    lay = ops.Layer.of(cfg)
+    idx, w = ops.route_noisy(lay, d["x"], d["w_router"], d["bias"], d["w_noise"], d["noise"])
+    pm = ops.permute(lay, idx, d["x"])
+    y_perm = ops.expert_ffn(lay, cfg.tokens, pm["offsets"], pm["x_perm"], d["w_gate"], d["w_up"],
+                            d["w_down"])
+    y_sh = ops.shared_ffn(lay, d["x"], d["ws_gate"], d["ws_up"], d["ws_down"]) if cfg.n_shared else None
+    y = ops.combine(lay, y_perm, pm["slot_row"], w, y_sh)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(idx), ref["topk_idx"])
+    check_y(host(y), ref["y"], cfg.dtype)
