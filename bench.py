@@ -42,7 +42,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 # rocprofv3 FETCH_SIZE (x2) and WRITE_SIZE (x1) in KiB, the factors taken from
 # a plain 1 GiB copy in the same run (profiles/grouped_gemm_gate_up_16b_fetch_write.md).
 # None whenever the kernel has changed since the counters were taken.
-TRAFFIC_BYTES = {"16b": (1915068 * 2 + 360448) * 1024}
+TRAFFIC_BYTES = {"16b": (1797775 * 2 + 360448) * 1024}
 
 
 def parse():
