@@ -12,12 +12,13 @@ constexpr int kDispatchMaxExperts = 256;
 
 // Stable counting sort of the T*K assignments of topk_idx (T <= kSmallTokens)
 // by expert, one thread per token: ballots give per-wave counts and in-wave
-// ranks; the scan runs over experts in LDS; a row is offsets[e] + rows of e
-// in earlier waves + rank in the wave, i.e. ascending token order.  Every
-// thread of the workgroup must call it.
+// ranks (only the wavefronts that hold tokens take part); the scan runs over
+// experts in LDS; a row is the first row of (wave, expert) - offsets[e] plus
+// the rows of e in earlier waves - plus the rank in the wave, i.e.
+// ascending token order.  Every thread of the workgroup must call it.
 struct SmallDispatchLds {
   uint64_t masks[kSmallTokens / kWave][kDispatchMaxExperts];
-  int cnt[kSmallTokens / kWave][kDispatchMaxExperts];
+  int cnt[kSmallTokens / kWave][kDispatchMaxExperts];   // then: first row of (wave, expert)
   int offs[kDispatchMaxExperts + 1];
 };
 
@@ -26,7 +27,7 @@ __device__ __forceinline__ void small_dispatch(const int32_t* __restrict__ idx, 
                                                int32_t* __restrict__ offsets,
                                                int32_t* __restrict__ row_token,
                                                int32_t* __restrict__ slot_row, SmallDispatchLds& sh) {
-  constexpr int NWV = kSmallTokens / kWave;
+  const int NWV = (T + kWave - 1) / kWave;   // wavefronts that hold tokens
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int t = threadIdx.x;
@@ -47,13 +48,15 @@ __device__ __forceinline__ void small_dispatch(const int32_t* __restrict__ idx, 
       bits3 |= (w == 3) ? b : 0ull;
     }
   }
-  for (int e = 0; e < Nr; ++e) {
-    const int w = e >> 6;
-    const uint64_t bits = (w == 0) ? bits0 : (w == 1) ? bits1 : (w == 2) ? bits2 : bits3;
-    const uint64_t m = __ballot((bits >> (e & 63)) & 1ull);
-    if (lane == 0) {
-      sh.masks[wave][e] = m;
-      sh.cnt[wave][e] = __popcll(m);
+  if (wave < NWV) {
+    for (int e = 0; e < Nr; ++e) {
+      const int w = e >> 6;
+      const uint64_t bits = (w == 0) ? bits0 : (w == 1) ? bits1 : (w == 2) ? bits2 : bits3;
+      const uint64_t m = __ballot((bits >> (e & 63)) & 1ull);
+      if (lane == 0) {
+        sh.masks[wave][e] = m;
+        sh.cnt[wave][e] = __popcll(m);
+      }
     }
   }
   __syncthreads();
@@ -61,7 +64,6 @@ __device__ __forceinline__ void small_dispatch(const int32_t* __restrict__ idx, 
   // in wavefront 0 (four experts per lane, shuffle prefix sums).
   if (threadIdx.x < Nr) {
     int c = 0;
-#pragma unroll
     for (int w = 0; w < NWV; ++w) c += sh.cnt[w][threadIdx.x];
     sh.offs[threadIdx.x + 1] = c;
   }
@@ -94,14 +96,24 @@ __device__ __forceinline__ void small_dispatch(const int32_t* __restrict__ idx, 
     offsets[e] = sh.offs[e];
     if (e < Nr) counts[e] = sh.offs[e + 1] - sh.offs[e];
   }
+  // First row of each (wavefront, expert): the expert's offset plus the
+  // rows of the wavefronts before (cnt is overwritten in place).
+  if (threadIdx.x < Nr) {
+    int run = sh.offs[threadIdx.x];
+    for (int w = 0; w < NWV; ++w) {
+      const int c = sh.cnt[w][threadIdx.x];
+      sh.cnt[w][threadIdx.x] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
   if (!valid) return;
   const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
   for (int j = 0; j < kDispatchMaxK; ++j) {
     if (j < K) {
       const int e = ids[j];
-      int r = sh.offs[e] + __popcll(sh.masks[wave][e] & below);
-      for (int w = 0; w < wave; ++w) r += sh.cnt[w][e];
+      const int r = sh.cnt[wave][e] + __popcll(sh.masks[wave][e] & below);
       slot_row[static_cast<int64_t>(t) * K + j] = r;
       row_token[r] = t;
     }
