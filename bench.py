@@ -261,6 +261,35 @@ def main():
                    + 4.0 * cfg.n_routed * dm + 2.0 * esz * T * dm)
     layer_gbs = layer_bytes / (ms * 1e-3) / 1e9
 
+    # The small memory-bound stages against HBM: their own algorithmic bytes
+    # over their event-timed stage time.
+    # rows the combine reads: routed, plus K_s folded shared rows or one y_shared row per token
+    R = P + (T * cfg.n_shared if fold else (T if cfg.n_shared > 0 else 0))
+    stage_bytes = {
+        "route": esz * T * dm + 4.0 * cfg.n_routed * dm + 8.0 * P,        # x, W_g, idx + weights
+        "dispatch": 4.0 * P + 8.0 * P + 8.0 * cfg.n_routed,              # idx; row_token, slot_row
+        "combine": esz * R * dm + 8.0 * P + esz * T * dm,               # rows, idx + weights, y
+    }
+    stage_hbm = {k: round(v / (st[k] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) for k, v in stage_bytes.items()}
+
+    # Cold memory-side cache: reading 512 MB between forwards evicts the
+    # 256 MB MALL with clean lines, so every weight comes from HBM (the timed
+    # steps above run back to back).
+    junk = torch.ones(128 << 20, dtype=torch.int32, device=dev)
+    sink = torch.empty((), dtype=torch.int64, device=dev)
+    cold = []
+    for _ in range(max(3, min(args.steps, 10))):
+        torch.sum(junk, dim=0, dtype=torch.int64, out=sink)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fwd(*call_args, checked=True)
+        b.record()
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b))
+    del junk, sink
+    cold_ms = float(np.median(cold))
+
     if args.copy_calibration:
         a = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
         b = torch.empty_like(a)
@@ -299,6 +328,10 @@ def main():
         "layer_algorithmic_bytes": layer_bytes,
         "layer_hbm_gbs": layer_gbs,
         "layer_hbm_frac": layer_gbs / PEAK_HBM_GBS,
+        "cold_mall_ms_per_step": cold_ms,
+        "cold_mall_layer_hbm_frac": layer_bytes / (cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "stage_algorithmic_bytes": stage_bytes,
+        "stage_hbm_frac": stage_hbm,
         "roofline": {
             "kernel": "gate/up grouped GEMM (grouped_gemm_bf16 gate/up, grouped; routed experts"
                       + (" + shared experts as extra groups)" if fold else ")"),
