@@ -488,11 +488,10 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
 #endif
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int STAGES>
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int MODE>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
-  constexpr int OUT_N = BN / 2;
-  const int out_n = (a.mode == kGateUp) ? OUT_N : BN;
-  const int n_ntiles = (a.N + out_n - 1) / out_n;
+  constexpr int OUT_N = (MODE == kGateUp) ? BN / 2 : BN;
+  const int n_ntiles = (a.N + OUT_N - 1) / OUT_N;
   int64_t max_mtiles;
   if (a.offsets == nullptr) {
     max_mtiles = (a.rows_total + BM - 1) / BM;
@@ -503,16 +502,17 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   const int64_t grid = max_mtiles * n_ntiles;
   if (grid == 0) return hipSuccess;
   const dim3 block(WM * WN * kWave);
-  const bool grouped = a.offsets != nullptr;
-  if (a.mode == kGateUp && grouped)
-    hipLaunchKernelGGL((grouped_gemm_bf16<BM, BN, WM, WN, BK, STAGES, kGateUp, true>), dim3(grid), block, 0, s, a);
-  else if (a.mode == kGateUp)
-    hipLaunchKernelGGL((grouped_gemm_bf16<BM, BN, WM, WN, BK, STAGES, kGateUp, false>), dim3(grid), block, 0, s, a);
-  else if (grouped)
-    hipLaunchKernelGGL((grouped_gemm_bf16<BM, BN, WM, WN, BK, STAGES, kDown, true>), dim3(grid), block, 0, s, a);
+  if (a.offsets != nullptr)
+    hipLaunchKernelGGL((grouped_gemm_bf16<BM, BN, WM, WN, BK, STAGES, MODE, true>), dim3(grid), block, 0, s, a);
   else
-    hipLaunchKernelGGL((grouped_gemm_bf16<BM, BN, WM, WN, BK, STAGES, kDown, false>), dim3(grid), block, 0, s, a);
+    hipLaunchKernelGGL((grouped_gemm_bf16<BM, BN, WM, WN, BK, STAGES, MODE, false>), dim3(grid), block, 0, s, a);
   return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN, int BK, int STAGES>
+hipError_t launch_both(const GemmArgs& a, hipStream_t s) {
+  return a.mode == kGateUp ? launch_cfg<BM, BN, WM, WN, BK, STAGES, kGateUp>(a, s)
+                           : launch_cfg<BM, BN, WM, WN, BK, STAGES, kDown>(a, s);
 }
 
 }  // namespace
@@ -520,12 +520,13 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.rows_total == 0) return hipSuccess;
   const int64_t mean_rows = a.rows_total / (a.offsets ? a.n_groups + a.n_extra : 1);
-  if (mean_rows >= 192) return launch_cfg<256, 256, 2, 4, 64, 2>(a, s);
-  if (mean_rows >= 64) return launch_cfg<128, 256, 2, 2, 64, 2>(a, s);
-  // Few rows per group: the weights stream through.  Down projections (the
-  // shorter K) use narrower tiles so that more of them run at once.
-  if (a.mode == kDown) return launch_cfg<32, 128, 1, 2, 64, 2>(a, s);
-  return launch_cfg<32, 256, 1, 4, 64, 2>(a, s);
+  if (mean_rows >= 192) return launch_both<256, 256, 2, 4, 64, 2>(a, s);
+  if (mean_rows >= 64) return launch_both<128, 256, 2, 2, 64, 2>(a, s);
+  // Few rows per group: the weights stream through and every workgroup's
+  // time is its share of them.  Narrow down tiles (64 columns) split the
+  // stream finer, so the last partial round of workgroups is short.
+  if (a.mode == kDown) return launch_cfg<32, 64, 1, 2, 64, 2, kDown>(a, s);
+  return launch_cfg<32, 256, 1, 4, 64, 2, kGateUp>(a, s);
 }
 
 }  // namespace moe
