@@ -57,7 +57,8 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = 1,          /* null required pointer, T < 0, bad enum, K' out of range,
-                                       negative capacity or group_size, bad ffn or bias_mode     */
+                                       negative capacity or group_size, bad ffn, bias_mode or
+                                       weight_layout                                             */
   MOE_ERR_UNSUPPORTED = 2,          /* shape/alignment outside the supported set above         */
   MOE_ERR_WORKSPACE_TOO_SMALL = 3,  /* ws_bytes below moe_workspace_size()                      */
   MOE_ERR_HIP = 4                   /* a HIP launch or query failed                              */
@@ -87,6 +88,20 @@ typedef enum {
      leaves the gate values unstated.                                      */
   MOE_BIAS_SELECTION = 1
 } moe_bias_mode;
+
+/* Storage order of the expert weights (w_gate, w_up, w_down, ws_*). */
+typedef enum {
+  /* [out_features, in_features] row-major, as described above.          */
+  MOE_WEIGHTS_ROW_MAJOR = 0,
+  /* The packed order written by moe_pack_weights (bf16 only): every matrix
+     is cut into 128-row tiles, and a tile stores its 64-wide K steps one
+     after another, each as 128 rows x 64 values row-major.  Element (n, k)
+     of an [N, K] matrix sits at (n/128)*128*K + (k/64)*128*64 +
+     (n%128)*64 + k%64.  A K step of a tile is then 16 KB of contiguous
+     memory, which the weight stream of the expert GEMMs reads faster.
+     Requires d % 128 == 0, I % 128 == 0 and I_s % 128 == 0.              */
+  MOE_WEIGHTS_PACKED = 1
+} moe_weight_layout;
 
 typedef enum {
   /* g_i = s_i on the top-K' of s = Softmax over N_r routed experts, not
@@ -122,6 +137,7 @@ typedef struct {
   int32_t group_size;   /* S, tokens per capacity group; 0 = all T     */
   int32_t ffn;          /* moe_ffn                                     */
   int32_t bias_mode;    /* moe_bias_mode                               */
+  int32_t weight_layout;/* moe_weight_layout                           */
 } moe_layer;
 
 int moe_abi_version(void);
@@ -153,6 +169,16 @@ int moe_route(const moe_layer* layer, int64_t T, const void* x, const float* w_r
 int moe_route_noisy(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
                     const float* logit_bias, const float* w_noise, const float* noise,
                     int32_t* topk_idx, float* topk_w, void* stream);
+
+/* Weight packing (once, before inference; no compute of the layer): dst =
+ * the MOE_WEIGHTS_PACKED form of `count` row-major bf16 matrices [rows,
+ * cols] at src (e.g. w_gate: count N_r, rows I, cols d; w_down: count N_r,
+ * rows d, cols I; ws_gate: count K_s, rows I_s, cols d).  dst has the same
+ * size and must not overlap src.  layer->dtype must be MOE_BF16; rows % 128
+ * == 0 and cols % 64 == 0, else MOE_ERR_UNSUPPORTED.  The other layer
+ * fields are checked as everywhere but not used. */
+int moe_pack_weights(const moe_layer* layer, int64_t count, int32_t rows, int32_t cols,
+                     const void* src, void* dst, void* stream);
 
 /* Floats written to `stats` by moe_route_stats for N_r experts, D groups. */
 #define MOE_STATS_LEN(n_routed, n_devices) (2 * (n_routed) + 2 * (n_devices) + 3)

@@ -6,6 +6,6 @@ ABI in include/moe.h; this package only marshals torch tensors to it.
 from . import ops  # noqa: F401
 from ._lib import LIB_PATH, MoeError, lib  # noqa: F401
 from .ops import (  # noqa: F401
-    Forward, Layer, combine, expert_ffn, forward, permute, route, route_noisy, route_stats, shared_ffn,
-    split_stats,
+    Forward, Layer, combine, expert_ffn, forward, pack_weights, permute, route, route_noisy, route_stats,
+    shared_ffn, split_stats,
 )

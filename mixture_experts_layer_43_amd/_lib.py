@@ -12,10 +12,11 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_GATE_SOFTMAX_TOPK, MOE_GATE_TOPK_SOFTMAX = 0, 1
 MOE_FFN_SILU_GATED, MOE_FFN_RELU = 0, 1
 MOE_BIAS_LOGITS, MOE_BIAS_SELECTION = 0, 1
+MOE_WEIGHTS_ROW_MAJOR, MOE_WEIGHTS_PACKED = 0, 1
 
 EXPORTS = (
     "moe_abi_version", "moe_status_str", "moe_last_hip_error", "moe_workspace_size",
-    "moe_route", "moe_route_noisy", "moe_route_stats", "moe_permute", "moe_expert_ffn", "moe_shared_ffn", "moe_combine",
+    "moe_pack_weights", "moe_route", "moe_route_noisy", "moe_route_stats", "moe_permute", "moe_expert_ffn", "moe_shared_ffn", "moe_combine",
     "moe_forward", "moe_forward_timed",
 )
 MOE_NUM_STAGES = 7
@@ -26,7 +27,7 @@ STAGES = ("route", "dispatch", "routed_gate_up", "routed_down", "shared_gate_up"
 class MoeLayer(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "d_model", "n_routed", "n_shared", "top_k", "d_ff", "d_ff_shared", "gate", "dtype",
-        "capacity", "group_size", "ffn", "bias_mode")]
+        "capacity", "group_size", "ffn", "bias_mode", "weight_layout")]
 
 
 class MoeError(RuntimeError):
@@ -50,6 +51,7 @@ _SIGS = {
     "moe_last_hip_error": ([], ctypes.c_int),
     "moe_workspace_size": ([LP, I64, ctypes.POINTER(SZ)], ctypes.c_int),
     "moe_route": ([LP, I64, P, P, P, P, P, P], ctypes.c_int),
+    "moe_pack_weights": ([LP, I64, ctypes.c_int32, ctypes.c_int32, P, P, P], ctypes.c_int),
     "moe_route_noisy": ([LP, I64, P, P, P, P, P, P, P, P], ctypes.c_int),
     "moe_route_stats": ([LP, I64, P, P, P, ctypes.c_int32, P, P, P, P, P, SZ, P], ctypes.c_int),
     "moe_permute": ([LP, I64, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),

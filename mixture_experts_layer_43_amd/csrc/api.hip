@@ -99,6 +99,8 @@ int check_layer(const moe_layer* L, int64_t T) {
   if (L->capacity < 0 || L->group_size < 0) return MOE_ERR_INVALID_ARG;
   if (L->ffn != MOE_FFN_SILU_GATED && L->ffn != MOE_FFN_RELU) return MOE_ERR_INVALID_ARG;
   if (L->bias_mode != MOE_BIAS_LOGITS && L->bias_mode != MOE_BIAS_SELECTION) return MOE_ERR_INVALID_ARG;
+  if (L->weight_layout != MOE_WEIGHTS_ROW_MAJOR && L->weight_layout != MOE_WEIGHTS_PACKED)
+    return MOE_ERR_INVALID_ARG;
   if (L->top_k < 1 || L->top_k > L->n_routed || L->top_k > 16) return MOE_ERR_INVALID_ARG;
   if (L->n_routed > 256) return MOE_ERR_UNSUPPORTED;
   if (T >= (int64_t{1} << 31) / 16) return MOE_ERR_UNSUPPORTED;
@@ -115,6 +117,13 @@ int check_layer(const moe_layer* L, int64_t T) {
   const int q = (L->dtype == MOE_BF16) ? 64 : 4;
   if (L->d_model % q != 0 || L->d_ff % q != 0) return MOE_ERR_UNSUPPORTED;
   if (L->n_shared > 0 && L->d_ff_shared % q != 0) return MOE_ERR_UNSUPPORTED;
+  if (L->weight_layout == MOE_WEIGHTS_PACKED) {
+    // Packed tiles are kPackRows rows of every expert matrix (I rows of W1/W3,
+    // d rows of W2) and bf16 only.
+    const int r = moe::kPackRows;
+    if (L->dtype != MOE_BF16 || L->d_model % r != 0 || L->d_ff % r != 0) return MOE_ERR_UNSUPPORTED;
+    if (L->n_shared > 0 && L->d_ff_shared % r != 0) return MOE_ERR_UNSUPPORTED;
+  }
   return MOE_OK;
 }
 
@@ -149,6 +158,7 @@ char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 // FFN ReLU(wi u) with wi in the W1 slot (one matrix, the plain GEMM with a
 // clamped epilogue).
 moe::GemmArgs first_projection(const moe_layer* L, moe::GemmArgs g) {
+  g.packed = L->weight_layout == MOE_WEIGHTS_PACKED;
   if (L->ffn == MOE_FFN_RELU) {
     g.mode = moe::kDown;
     g.relu = true;
@@ -206,6 +216,7 @@ moe::GemmArgs routed_down(const moe_layer* L, int64_t T, const int32_t* offsets,
   g.C = y_perm;
   g.ldc = L->d_model;
   g.mode = moe::kDown;
+  g.packed = L->weight_layout == MOE_WEIGHTS_PACKED;
   return g;
 }
 
@@ -275,6 +286,7 @@ moe::GemmArgs shared_down(const moe_layer* L, int64_t T, const void* h_shared,
   h.C = y_shared;
   h.ldc = L->d_model;
   h.mode = moe::kDown;
+  h.packed = L->weight_layout == MOE_WEIGHTS_PACKED;
   return h;
 }
 
@@ -356,6 +368,20 @@ static moe::RouteArgs route_args(const moe_layer* layer, int64_t T, const void* 
 int moe_route(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
               const float* logit_bias, int32_t* topk_idx, float* topk_w, void* stream) {
   return route_impl(layer, T, x, w_router, logit_bias, topk_idx, topk_w, nullptr, stream);
+}
+
+int moe_pack_weights(const moe_layer* layer, int64_t count, int32_t rows, int32_t cols,
+                     const void* src, void* dst, void* stream) {
+  MOE_TRY(check_layer(layer, 0));
+  if (count < 0 || rows <= 0 || cols <= 0 || src == dst) return MOE_ERR_INVALID_ARG;
+  if (layer->dtype != MOE_BF16 || rows % moe::kPackRows != 0 || cols % 64 != 0)
+    return MOE_ERR_UNSUPPORTED;
+  if (count * rows * static_cast<int64_t>(cols) * 2 >= (int64_t{1} << 40)) return MOE_ERR_UNSUPPORTED;
+  if (count == 0) return MOE_OK;
+  MOE_TRY(need(src));
+  MOE_TRY(need(dst));
+  MOE_HIP(moe::launch_pack(src, dst, count, rows, cols, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
 }
 
 int moe_route_noisy(const moe_layer* layer, int64_t T, const void* x, const float* w_router,

@@ -103,12 +103,16 @@ __device__ __forceinline__ void lds_barrier() {
 template <int BM, int BK, int A_LD, int B_LD>
 __device__ __forceinline__ void copy_step(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                           const uint32_t (&a_off)[A_LD], const uint32_t (&b_off)[B_LD],
-                                          int k, int k_sub, int64_t b_sub_stride, int wv,
-                                          bf16_t* __restrict__ s) {
+                                          int k, int k_sub, int64_t b_sub_stride, bool packed,
+                                          int wv, bf16_t* __restrict__ s) {
   constexpr int R = kWave / (BK / 8);
   const uint32_t sa = static_cast<uint32_t>(k) * 2u;
+  // Row-major B: column k of the K run.  Packed B (kPackRows-row tiles, each
+  // a sequence of 64-wide K steps): the step's block inside the tile.
+  const int kin = k % k_sub;
+  const int64_t kpos = packed ? static_cast<int64_t>(kin / 64) * (kPackRows * 64) : kin;
   const uint32_t sb = static_cast<uint32_t>(
-      (static_cast<int64_t>(k / k_sub) * b_sub_stride + (k % k_sub)) * 2);
+      (static_cast<int64_t>(k / k_sub) * b_sub_stride + kpos) * 2);
 #pragma unroll
   for (int i = 0; i < A_LD; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds_ptr(s + (wv * A_LD + i) * R * BK), 16, a_off[i],
@@ -202,7 +206,8 @@ template <int BM, int BK, int STAGES, int MB, int NB, int MBA, int A_LD, int B_L
 __device__ __forceinline__ void k_loop(f32x16 (&acc)[MB][NB], __amdgpu_buffer_rsrc_t ra,
                                        __amdgpu_buffer_rsrc_t rb, const uint32_t (&a_off)[A_LD],
                                        const uint32_t (&b_off)[B_LD], int nk, int k_sub,
-                                       int64_t kstride_b, int wv, int khalf, const int (&a_row)[MB],
+                                       int64_t kstride_b, bool packed, int wv, int khalf,
+                                       const int (&a_row)[MB],
                                        const int (&b_row)[NB], bf16_t* smem, int se) {
   constexpr int L = A_LD + B_LD;
   Frags<MB, NB> fr;
@@ -211,7 +216,7 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[MB][NB], __amdgpu_buffer_rs
     lds_barrier();
     const int kn = kt + STAGES - 1;
     if (kn < nk)
-      copy_step<BM, BK, A_LD, B_LD>(ra, rb, a_off, b_off, kn * BK, k_sub, kstride_b, wv,
+      copy_step<BM, BK, A_LD, B_LD>(ra, rb, a_off, b_off, kn * BK, k_sub, kstride_b, packed, wv,
                                     smem + (kn % STAGES) * se);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (MBA > 0)
@@ -379,7 +384,10 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
     const int c = lp ^ swz<BK>(r);
     int n = nt * OUT_N + ((MODE == kGateUp && up) ? r - BN / 2 : r);
     n = min(n, p.N - 1);
-    b_off[i] = static_cast<uint32_t>((static_cast<int64_t>(n) * p.ldb + c * 8) * 2);
+    const int64_t e = p.packed ? static_cast<int64_t>(n / kPackRows) * kPackRows * p.k_sub +
+                                     (n % kPackRows) * 64 + c * 8
+                               : static_cast<int64_t>(n) * p.ldb + c * 8;
+    b_off[i] = static_cast<uint32_t>(e * 2);
   }
   static_assert(MODE == kDown || (BN / 2) % (RPL * B_LD) == 0, "B rows of a wavefront straddle W1/W3");
 
@@ -413,12 +421,13 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
   const int64_t kstride_b = p.b_sub_stride;
 #pragma unroll
   for (int j = 0; j < STAGES - 1; ++j)
-    if (j < nk) copy_step<BM, BK, A_LD, B_LD>(ra, rb, a_off, b_off, j * BK, p.k_sub, kstride_b, wv,
+    if (j < nk) copy_step<BM, BK, A_LD, B_LD>(ra, rb, a_off, b_off, j * BK, p.k_sub, kstride_b, p.packed, wv,
                                                smem + j * SE);
   // 32-row blocks of this wavefront that hold rows of the tile.
   const int mba = __builtin_amdgcn_readfirstlane(max(0, min(MB, (rows - wm * TM + 31) / 32)));
 #define MOE_K_LOOP(n)                                                                            \
   k_loop<BM, BK, STAGES, MB, NB, n, A_LD, B_LD>(acc, ra, rb, a_off, b_off, nk, p.k_sub, kstride_b, \
+                                                p.packed, \
                                                 wv, khalf, a_row, b_row, smem, SE)
   if (mba == MB) {
     MOE_K_LOOP(MB);
@@ -490,6 +499,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
 
 template <int BM, int BN, int WM, int WN, int BK, int STAGES, int MODE>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
+  static_assert(BK == 64, "the packed weight layout has 64-wide K steps");
   constexpr int OUT_N = (MODE == kGateUp) ? BN / 2 : BN;
   const int n_ntiles = (a.N + OUT_N - 1) / OUT_N;
   int64_t max_mtiles;
@@ -515,7 +525,30 @@ hipError_t launch_both(const GemmArgs& a, hipStream_t s) {
                            : launch_cfg<BM, BN, WM, WN, BK, STAGES, kDown>(a, s);
 }
 
+// One 16-byte chunk (8 consecutive k of one row) per thread.
+__global__ __launch_bounds__(256) void pack_kernel(const uint4* __restrict__ src,
+                                                   uint4* __restrict__ dst, int64_t chunks,
+                                                   int rows, int cols) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= chunks) return;
+  const int64_t per_row = cols / 8, per_mat = static_cast<int64_t>(rows) * per_row;
+  const int64_t g = i / per_mat, rem = i % per_mat;
+  const int64_t n = rem / per_row, k = (rem % per_row) * 8;
+  const int64_t e = g * rows * static_cast<int64_t>(cols) + (n / kPackRows) * kPackRows * cols +
+                    (k / 64) * (kPackRows * 64) + (n % kPackRows) * 64 + k % 64;
+  dst[e / 8] = src[i];
+}
+
 }  // namespace
+
+hipError_t launch_pack(const void* src, void* dst, int64_t count, int rows, int cols,
+                       hipStream_t s) {
+  const int64_t chunks = count * rows * static_cast<int64_t>(cols) / 8;
+  if (chunks == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_kernel, dim3(static_cast<unsigned>((chunks + 255) / 256)), dim3(256), 0,
+                     s, static_cast<const uint4*>(src), static_cast<uint4*>(dst), chunks, rows, cols);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.rows_total == 0) return hipSuccess;

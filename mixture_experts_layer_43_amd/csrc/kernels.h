@@ -74,6 +74,16 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
 // ---- grouped GEMMs (gemm_bf16.hip, gemm_f32.hip) ----
 enum GemmMode { kGateUp = 0, kDown = 1 };
 
+// Packed weight layout (bf16): a [N, K] matrix is cut into tiles of
+// kPackRows rows (N % kPackRows == 0); a tile holds its K/64 steps one after
+// the other, each step kPackRows rows x 64 values, row-major.  Element (n, k)
+// sits at (n / kPackRows) * kPackRows * K + (k / 64) * kPackRows * 64 +
+// (n % kPackRows) * 64 + k % 64, so one K step of a tile is 16 KB of
+// contiguous memory.
+constexpr int kPackRows = 128;
+// dst = the packed form of `count` row-major [rows, cols] bf16 matrices.
+hipError_t launch_pack(const void* src, void* dst, int64_t count, int rows, int cols, hipStream_t s);
+
 // Rows of group g are [offsets[g], offsets[g+1]) of a row-concatenated
 // matrix (offsets null: one group of M rows).  A row r lives at
 // A + (gather ? gather[r] : r) * lda.  B element (n, k) of group g is
@@ -88,6 +98,7 @@ enum GemmMode { kGateUp = 0, kDown = 1 };
 // row r reads A row (r - extra_base) % extra_rows (every token once).
 struct GemmArgs {
   bool relu;               // kDown only: C[r, n] = max(A_r . B0_n, 0) (ReLU expert FFN)
+  bool packed;             // B (and Bx) in the packed layout (bf16 only; k_sub is the K of one matrix)
   int64_t a_bytes;         // bytes of A readable through row indices (< 4 GB)
   int64_t b_bytes;         // bytes of one group's B0 (and of its B1) (< 4 GB)
   const int32_t* offsets;

@@ -20,6 +20,7 @@ _DT = {"f32": (_lib.MOE_F32, torch.float32), "bf16": (_lib.MOE_BF16, torch.bfloa
 _GATE = {"softmax_topk": _lib.MOE_GATE_SOFTMAX_TOPK, "topk_softmax": _lib.MOE_GATE_TOPK_SOFTMAX}
 _FFN = {"silu": _lib.MOE_FFN_SILU_GATED, "relu": _lib.MOE_FFN_RELU}
 _BIAS = {"logits": _lib.MOE_BIAS_LOGITS, "selection": _lib.MOE_BIAS_SELECTION}
+_LAYOUT = {"row_major": _lib.MOE_WEIGHTS_ROW_MAJOR, "packed": _lib.MOE_WEIGHTS_PACKED}
 
 
 @dataclass(frozen=True)
@@ -38,13 +39,14 @@ class Layer:
     group_size: int = 0     # tokens per capacity group; 0 = the whole batch
     ffn: str = "silu"       # "silu" (W1, W3, W2) or "relu" (wi = w_gate, wo = w_down)
     bias_mode: str = "logits"  # "logits": bias in selection and gates; "selection": selection only
+    weight_layout: str = "row_major"  # or "packed" (weights converted by pack_weights)
 
     @classmethod
     def of(cls, cfg) -> "Layer":
         return cls(cfg.d_model, cfg.n_routed, cfg.n_shared, cfg.top_k, cfg.d_ff,
                    cfg.d_ff_shared, cfg.gate, cfg.dtype, getattr(cfg, "capacity", 0),
                    getattr(cfg, "group_size", 0), getattr(cfg, "ffn", "silu"),
-                   getattr(cfg, "bias_mode", "logits"))
+                   getattr(cfg, "bias_mode", "logits"), getattr(cfg, "weight_layout", "row_major"))
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -53,7 +55,8 @@ class Layer:
     def c(self) -> MoeLayer:
         return MoeLayer(self.d_model, self.n_routed, self.n_shared, self.top_k, self.d_ff,
                         self.d_ff_shared, _GATE[self.gate], _DT[self.dtype][0], self.capacity,
-                        self.group_size, _FFN[self.ffn], _BIAS[self.bias_mode])
+                        self.group_size, _FFN[self.ffn], _BIAS[self.bias_mode],
+                        _LAYOUT[self.weight_layout])
 
 
 def _p(t):
@@ -116,6 +119,18 @@ def route_noisy(layer: Layer, x, w_router, bias, w_noise, noise):
     call("moe_route_noisy", ctypes.byref(layer.c()), T, _p(x), _p(w_router), _p(bias), _p(w_noise),
          _p(noise), _p(idx), _p(w), _stream())
     return idx, w
+
+
+def pack_weights(layer: Layer, w):
+    """The packed copy of a [count, rows, cols] (or [rows, cols]) bf16 weight tensor."""
+    if w is None:
+        return None
+    if w.dtype != torch.bfloat16 or not w.is_cuda or not w.is_contiguous() or w.dim() not in (2, 3):
+        raise ValueError("pack_weights: need a contiguous bf16 GPU tensor of rank 2 or 3")
+    count, rows, cols = (1, *w.shape) if w.dim() == 2 else tuple(w.shape)
+    out = torch.empty_like(w)
+    call("moe_pack_weights", ctypes.byref(layer.c()), count, rows, cols, _p(w), _p(out), _stream())
+    return out
 
 
 def stats_len(layer: Layer, n_devices: int) -> int:

@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     L = _lib.lib()
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib.EXPORTS)
@@ -79,6 +79,10 @@ def test_workspace_size_scales_with_tokens():
     (dict(capacity=-1), 8, MOE_ERR_INVALID_ARG),
     (dict(group_size=-3), 8, MOE_ERR_INVALID_ARG),
     (dict(capacity=5, group_size=64), 8, MOE_OK),
+    (dict(weight_layout=1), 8, MOE_OK),                            # d, I, I_s multiples of 128
+    (dict(weight_layout=1, d_ff=1344, d_ff_shared=1344), 8, MOE_ERR_UNSUPPORTED),
+    (dict(weight_layout=1, dtype=MOE_F32), 8, MOE_ERR_UNSUPPORTED),
+    (dict(weight_layout=5), 8, MOE_ERR_INVALID_ARG),
 ])
 def test_layer_validation(kw, T, want):
     st, _ = ws_size(layer(**kw), T)
@@ -111,6 +115,21 @@ def test_capacity_workspace():
     P, Nr = 4096 * 6, 64
     assert one >= base + 2 * P * 4 + (2 * Nr + 1) * 4
     assert many - one >= (256 - 1) * 2 * Nr * 4
+
+
+def test_pack_weights_argument_errors():
+    L = _lib.lib()
+    lay = layer()
+    P = ctypes.c_void_p
+    a, b = P(FAKE), P(FAKE + 4096)
+    assert L.moe_pack_weights(ctypes.byref(lay), 2, 100, 64, a, b, None) == MOE_ERR_UNSUPPORTED
+    assert L.moe_pack_weights(ctypes.byref(lay), 2, 128, 96, a, b, None) == MOE_ERR_UNSUPPORTED
+    assert L.moe_pack_weights(ctypes.byref(lay), 2, 128, 64, a, a, None) == MOE_ERR_INVALID_ARG
+    assert L.moe_pack_weights(ctypes.byref(lay), -1, 128, 64, a, b, None) == MOE_ERR_INVALID_ARG
+    assert L.moe_pack_weights(ctypes.byref(lay), 2, 128, 64, None, b, None) == MOE_ERR_INVALID_ARG
+    f32 = layer(dtype=MOE_F32, d_model=64, d_ff=64, d_ff_shared=64)
+    assert L.moe_pack_weights(ctypes.byref(f32), 2, 128, 64, a, b, None) == MOE_ERR_UNSUPPORTED
+    assert L.moe_pack_weights(ctypes.byref(lay), 0, 128, 64, a, b, None) == MOE_OK   # nothing to do
 
 
 def test_route_stats_argument_errors():
