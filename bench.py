@@ -5,7 +5,10 @@
 
 A step is one moe_forward (router, dispatch, routed gate/up and down grouped
 GEMMs, shared experts, combine) over one batch of seeded synthetic inputs
-that are resident in HBM before timing starts.  The timed steps run through
+that are resident in HBM before timing starts.  By default the expert
+weights are converted once to the packed layout (moe_pack_weights) before
+timing, as a server would at load time; --weights row_major times the plain
+layout, and the JSON line carries the other layout's time beside it.  The timed steps run through
 moe_forward_timed with a HIP event pair around the gate/up kernel only (on
 the launch stream); the per-stage breakdown comes from a few further steps
 with every marker set, outside the timed region.
@@ -38,11 +41,13 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
-# HBM bytes per launch of the routed gate/up kernel on the 16b layer, from
-# rocprofv3 FETCH_SIZE (x2) and WRITE_SIZE (x1) in KiB, the factors taken from
-# a plain 1 GiB copy in the same run (profiles/grouped_gemm_gate_up_16b_fetch_write.md).
-# None whenever the kernel has changed since the counters were taken.
-TRAFFIC_BYTES = {"16b": (1797775 * 2 + 360448) * 1024}
+# HBM bytes per launch of the routed gate/up kernel, by (layer, weight layout),
+# from rocprofv3 FETCH_SIZE (x2) and WRITE_SIZE (x1) in KiB, the factors taken
+# from a plain 1 GiB copy in the same run
+# (profiles/grouped_gemm_gate_up_16b_fetch_write.md).  None whenever the
+# kernel has changed since the counters were taken.
+TRAFFIC_BYTES = {("16b", "packed"): (1833556 * 2 + 360448) * 1024,
+                 ("16b", "row_major"): (1797775 * 2 + 360448) * 1024}
 
 
 def parse():
@@ -51,6 +56,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="16b", help="layer shape from synth.configs")
+    ap.add_argument("--weights", choices=("packed", "row_major"), default="packed",
+                    help="expert weight layout the timed forward reads (packed: converted once by "
+                         "moe_pack_weights before timing, like loading a checkpoint)")
     ap.add_argument("--cpu-tokens", type=int, default=8192,
                     help="tokens of the workload the oracle is timed on (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -117,12 +125,20 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] inputs for {cfg.name} ready in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
 
-    lay = ops.Layer.of(cfg)
+    lay_rm = ops.Layer.of(cfg)
+    weight_keys = ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")
+    packable = cfg.dtype == "bf16" and all(v % 128 == 0 for v in (cfg.d_model, cfg.d_ff, cfg.d_ff_shared))
+    layout = args.weights if packable else "row_major"
+    rm_args = [d["x"], d["w_router"], d["bias"], *[d[k] for k in weight_keys]]
+    if layout == "packed":
+        lay = dataclasses.replace(lay_rm, weight_layout="packed")
+        pk = {k: ops.pack_weights(lay_rm, d[k]) for k in weight_keys}
+        call_args = [d["x"], d["w_router"], d["bias"], *[pk[k] for k in weight_keys]]
+    else:
+        lay = lay_rm
+        call_args = rm_args
     fwd = ops.Forward(lay, cfg.tokens, dev)
-    fwd.check(d["x"], d["w_router"], d["bias"], d["w_gate"], d["w_up"], d["w_down"],
-              d["ws_gate"], d["ws_up"], d["ws_down"], None)
-    call_args = [d["x"], d["w_router"], d["bias"], d["w_gate"], d["w_up"], d["w_down"],
-                 d["ws_gate"], d["ws_up"], d["ws_down"]]
+    fwd.check(*call_args, None)
 
     for _ in range(args.warmup):
         fwd(*call_args, checked=True)
@@ -156,9 +172,8 @@ def main():
 
     def step(arr):
         _lib.check("moe_forward_timed", lib.moe_forward_timed(
-            ctypes.byref(c_layer), cfg.tokens, p(d["x"]), p(d["w_router"]), p(d["bias"]),
-            p(d["w_gate"]), p(d["w_up"]), p(d["w_down"]), p(d["ws_gate"]), p(d["ws_up"]),
-            p(d["ws_down"]), None, p(fwd.y), p(fwd.topk_idx), p(fwd.topk_w), p(fwd.counts),
+            ctypes.byref(c_layer), cfg.tokens, *[p(a) for a in call_args], None, p(fwd.y),
+            p(fwd.topk_idx), p(fwd.topk_w), p(fwd.counts),
             p(fwd.offsets), p(fwd.ws), fwd.ws.numel(), stream, arr))
 
     # Timed region: whole-layer steps; HIP events mark only the gate/up kernel.
@@ -216,6 +231,19 @@ def main():
 
     route_ms = per_call_ms(route_plain)
     route_stats_ms = per_call_ms(route_with_stats)
+
+    # The other weight layout on the same batch (row-major when the timed
+    # forward reads packed weights).
+    other = "row_major" if layout == "packed" else ("packed" if packable else None)
+    other_ms = None
+    if other is not None:
+        lay_o = dataclasses.replace(lay_rm, weight_layout=other)
+        o_args = rm_args if other == "row_major" else \
+            [d["x"], d["w_router"], d["bias"], *[ops.pack_weights(lay_rm, d[k]) for k in weight_keys]]
+        fo = ops.Forward(lay_o, cfg.tokens, dev)
+        other_ms = per_call_ms(lambda: fo(*o_args, checked=True), n=max(3, min(args.steps, 10)))
+        del fo, o_args
+        torch.cuda.empty_cache()
 
     # Expert capacity (Switch/GShard, one group of the whole batch): the same
     # layer with C = ceil(factor * T * K' / N_r) slots per expert.
@@ -317,6 +345,7 @@ def main():
                         f"SiLU FFN width {I}, {cfg.gate}",
             "tokens": T, "d_model": dm, "n_routed": cfg.n_routed, "n_shared": cfg.n_shared,
             "top_k": K, "d_ff": I, "gate": cfg.gate, "parallelism": "single GPU",
+            "weights": layout,
         },
         "expert_gemm_tflops": expert_tflops,
         "expert_gemm_frac_mfma": expert_tflops / PEAK_BF16_TFLOPS,
@@ -325,6 +354,8 @@ def main():
         "routing_stats": {"route_ms": route_ms, "route_stats_ms": route_stats_ms,
                           "n_devices": n_dev},
         "capacity": capacity,
+        "weights": layout,
+        "other_layout": {"weights": other, "ms_per_step": other_ms},
         "layer_algorithmic_bytes": layer_bytes,
         "layer_hbm_gbs": layer_gbs,
         "layer_hbm_frac": layer_gbs / PEAK_HBM_GBS,
@@ -340,7 +371,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS if mfma_bound else PEAK_HBM_GBS,
             "unit": "TFLOP/s" if mfma_bound else "GB/s",
             "frac": gu_tflops / PEAK_BF16_TFLOPS if mfma_bound else gu_gbs / PEAK_HBM_GBS,
-            "traffic": TRAFFIC_BYTES.get(cfg.name),
+            "traffic": TRAFFIC_BYTES.get((cfg.name, layout)),
             "algorithmic_flop_per_launch": gu_flop,
             "algorithmic_bytes_per_launch": gu_bytes,
             "avg_launch_ms": gu_ms,
