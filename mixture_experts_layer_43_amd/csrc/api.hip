@@ -373,11 +373,12 @@ int moe_route(const moe_layer* layer, int64_t T, const void* x, const float* w_r
 int moe_pack_weights(const moe_layer* layer, int64_t count, int32_t rows, int32_t cols,
                      const void* src, void* dst, void* stream) {
   MOE_TRY(check_layer(layer, 0));
-  if (count < 0 || rows <= 0 || cols <= 0 || src == dst) return MOE_ERR_INVALID_ARG;
+  if (count < 0 || rows <= 0 || cols <= 0) return MOE_ERR_INVALID_ARG;
   if (layer->dtype != MOE_BF16 || rows % moe::kPackRows != 0 || cols % 64 != 0)
     return MOE_ERR_UNSUPPORTED;
   if (count * rows * static_cast<int64_t>(cols) * 2 >= (int64_t{1} << 40)) return MOE_ERR_UNSUPPORTED;
-  if (count == 0) return MOE_OK;
+  if (count == 0) return MOE_OK;   // e.g. the shared weights of a layer with K_s = 0
+  if (src == dst) return MOE_ERR_INVALID_ARG;
   MOE_TRY(need(src));
   MOE_TRY(need(dst));
   MOE_HIP(moe::launch_pack(src, dst, count, rows, cols, static_cast<hipStream_t>(stream)));

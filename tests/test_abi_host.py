@@ -130,6 +130,7 @@ def test_pack_weights_argument_errors():
     f32 = layer(dtype=MOE_F32, d_model=64, d_ff=64, d_ff_shared=64)
     assert L.moe_pack_weights(ctypes.byref(f32), 2, 128, 64, a, b, None) == MOE_ERR_UNSUPPORTED
     assert L.moe_pack_weights(ctypes.byref(lay), 0, 128, 64, a, b, None) == MOE_OK   # nothing to do
+    assert L.moe_pack_weights(ctypes.byref(lay), 0, 128, 64, None, None, None) == MOE_OK
 
 
 def test_route_stats_argument_errors():
