@@ -9,9 +9,10 @@ that are resident in HBM before timing starts.  By default the expert
 weights are converted once to the packed layout (moe_pack_weights) before
 timing, as a server would at load time; --weights row_major times the plain
 layout, and the JSON line carries the other layout's time beside it.  The timed steps run through
-moe_forward_timed with a HIP event pair around the gate/up kernel only (on
-the launch stream); the per-stage breakdown comes from a few further steps
-with every marker set, outside the timed region.
+moe_forward_timed with a HIP event pair for the gate/up kernel only, bound
+to its launch on the launch stream (the kernel's own start and end); the
+per-stage breakdown comes from a few further steps with every marker set,
+outside the timed region.
 
 Prints one JSON line.  `roofline` is for the dominant kernel, the gate/up
 grouped GEMM, whose launch does 4*R*d*I FLOPs (R = T*K' routed rows, plus
@@ -46,8 +47,8 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 # from a plain 1 GiB copy in the same run
 # (profiles/grouped_gemm_gate_up_16b_fetch_write.md).  None whenever the
 # kernel has changed since the counters were taken.
-TRAFFIC_BYTES = {("16b", "packed"): (1833556 * 2 + 360448) * 1024,
-                 ("16b", "row_major"): (1797775 * 2 + 360448) * 1024}
+TRAFFIC_BYTES = {("16b", "packed"): (1768585 * 2 + 360448) * 1024,
+                 ("16b", "row_major"): (1812059 * 2 + 360448) * 1024}
 
 
 def parse():

@@ -280,12 +280,16 @@ enum {
 };
 
 /* moe_forward with per-stage timing markers, for measurement.  `events`
- * holds 2*MOE_NUM_STAGES hipEvent_t handles (as void*) created by the caller;
- * events[2s] and events[2s+1] are recorded on `stream` right before and
- * right after stage s, so hipEventElapsedTime(events[2s], events[2s+1]) is
- * that stage's GPU time.  A NULL handle skips that marker (to time only
- * some stages); a NULL array is MOE_ERR_INVALID_ARG.  Everything else is
- * exactly moe_forward. */
+ * holds 2*MOE_NUM_STAGES hipEvent_t handles (as void*) created by the caller
+ * (with timing enabled); hipEventElapsedTime(events[2s], events[2s+1]) is
+ * stage s's GPU time.  The four GEMM stages are one kernel launch each
+ * (bf16 layers), and their two events are bound to that launch
+ * (hipExtLaunchKernel): they take the kernel's own start and end, and add
+ * no marker between the kernels.  The other stages, the GEMM stages of fp32
+ * layers and GEMM stages with nothing to launch have their events recorded
+ * on `stream` right before and right after the stage.  A NULL handle skips
+ * that marker (to time only some stages); a NULL array is
+ * MOE_ERR_INVALID_ARG.  Everything else is exactly moe_forward. */
 int moe_forward_timed(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
                       const float* logit_bias, const void* w_gate, const void* w_up,
                       const void* w_down, const void* ws_gate, const void* ws_up,

@@ -236,8 +236,14 @@ void add_shared_groups(const moe_layer* L, int64_t T, moe::GemmArgs& g, const vo
   if (down) g.a_bytes = g.rows_total * static_cast<int64_t>(L->d_ff) * e;
 }
 
-int gemm(const moe_layer* L, const moe::GemmArgs& g, hipStream_t s) {
-  MOE_HIP(L->dtype == MOE_BF16 ? moe::launch_gemm_bf16(g, s) : moe::launch_gemm_f32(g, s));
+int gemm(const moe_layer* L, const moe::GemmArgs& g, hipStream_t s, moe::StageEvents ev = {}) {
+  if (L->dtype == MOE_BF16) {
+    MOE_HIP(moe::launch_gemm_bf16(g, s, ev));
+    return MOE_OK;
+  }
+  if (ev.start != nullptr) MOE_HIP(hipEventRecord(ev.start, s));
+  MOE_HIP(moe::launch_gemm_f32(g, s));
+  if (ev.stop != nullptr) MOE_HIP(hipEventRecord(ev.stop, s));
   return MOE_OK;
 }
 
@@ -297,6 +303,15 @@ struct Marks {
   int mark(int i) const {
     if (ev != nullptr && ev[i] != nullptr) MOE_HIP(hipEventRecord(ev[i], s));
     return MOE_OK;
+  }
+  // Stage `st` as one kernel launch that carries its own start/end events.
+  moe::StageEvents launch(int st) const {
+    moe::StageEvents e;
+    if (ev != nullptr) {
+      e.start = ev[2 * st];
+      e.stop = ev[2 * st + 1];
+    }
+    return e;
   }
 };
 
@@ -624,20 +639,16 @@ static int forward_impl(const moe_layer* layer, int64_t T, const void* x,
     add_shared_groups(layer, T, gu, ws_gate, ws_up, false);
     add_shared_groups(layer, T, dn, ws_down, nullptr, true);
   }
-  MOE_TRY(m.mark(4));
-  MOE_TRY(gemm(layer, gu, s));
-  MOE_TRY(m.mark(5));
-  MOE_TRY(m.mark(6));
-  MOE_TRY(gemm(layer, dn, s));
-  MOE_TRY(m.mark(7));
-  MOE_TRY(m.mark(8));
-  if (layer->n_shared > 0 && !fold)
-    MOE_TRY(gemm(layer, shared_gate_up(layer, T, x, ws_gate, ws_up, h_shared), s));
-  MOE_TRY(m.mark(9));
-  MOE_TRY(m.mark(10));
-  if (layer->n_shared > 0 && !fold)
-    MOE_TRY(gemm(layer, shared_down(layer, T, h_shared, ws_down, y_shared), s));
-  MOE_TRY(m.mark(11));
+  // Each GEMM stage is one launch; its events time the kernel itself.
+  MOE_TRY(gemm(layer, gu, s, m.launch(2)));
+  MOE_TRY(gemm(layer, dn, s, m.launch(3)));
+  if (layer->n_shared > 0 && !fold) {
+    MOE_TRY(gemm(layer, shared_gate_up(layer, T, x, ws_gate, ws_up, h_shared), s, m.launch(4)));
+    MOE_TRY(gemm(layer, shared_down(layer, T, h_shared, ws_down, y_shared), s, m.launch(5)));
+  } else {
+    MOE_HIP(moe::record_stage(m.launch(4), s));
+    MOE_HIP(moe::record_stage(m.launch(5), s));
+  }
   MOE_TRY(m.mark(12));
   moe::CombineArgs c{};
   c.y_perm = y_perm;

@@ -18,6 +18,8 @@
 // distinct banks) -> v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  Workgroup ids are remapped so that consecutive tiles run on
 // the same XCD and share its L2.
 #include "common.h"
+#include <hip/hip_ext.h>
+
 #include "kernels.h"
 
 namespace moe {
@@ -108,9 +110,10 @@ __device__ __forceinline__ void copy_step(__amdgpu_buffer_rsrc_t ra, __amdgpu_bu
   constexpr int R = kWave / (BK / 8);
   const uint32_t sa = static_cast<uint32_t>(k) * 2u;
   // Row-major B: column k of the K run.  Packed B (kPackRows-row tiles, each
-  // a sequence of 64-wide K steps): the step's block inside the tile.
+  // a sequence of 64-wide K steps): the step's block inside the tile, plus
+  // the column inside the step when BK = 32.
   const int kin = k % k_sub;
-  const int64_t kpos = packed ? static_cast<int64_t>(kin / 64) * (kPackRows * 64) : kin;
+  const int64_t kpos = packed ? static_cast<int64_t>(kin / 64) * (kPackRows * 64) + kin % 64 : kin;
   const uint32_t sb = static_cast<uint32_t>(
       (static_cast<int64_t>(k / k_sub) * b_sub_stride + kpos) * 2);
 #pragma unroll
@@ -498,8 +501,8 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
 }
 
 template <int BM, int BN, int WM, int WN, int BK, int STAGES, int MODE>
-hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
-  static_assert(BK == 64, "the packed weight layout has 64-wide K steps");
+hipError_t launch_cfg(const GemmArgs& a, hipStream_t s, StageEvents ev) {
+  static_assert(BK == 32 || BK == 64, "K steps divide the packed layout's 64-wide steps");
   constexpr int OUT_N = (MODE == kGateUp) ? BN / 2 : BN;
   const int n_ntiles = (a.N + OUT_N - 1) / OUT_N;
   int64_t max_mtiles;
@@ -510,19 +513,21 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
     max_mtiles = (a.rows_total + static_cast<int64_t>(a.n_groups + a.n_extra) * (BM - 1)) / BM;
   }
   const int64_t grid = max_mtiles * n_ntiles;
-  if (grid == 0) return hipSuccess;
+  if (grid == 0) return record_stage(ev, s);
   const dim3 block(WM * WN * kWave);
   if (a.offsets != nullptr)
-    hipLaunchKernelGGL((grouped_gemm_bf16<BM, BN, WM, WN, BK, STAGES, MODE, true>), dim3(grid), block, 0, s, a);
+    hipExtLaunchKernelGGL((grouped_gemm_bf16<BM, BN, WM, WN, BK, STAGES, MODE, true>), dim3(grid), block, 0,
+                          s, ev.start, ev.stop, 0, a);
   else
-    hipLaunchKernelGGL((grouped_gemm_bf16<BM, BN, WM, WN, BK, STAGES, MODE, false>), dim3(grid), block, 0, s, a);
+    hipExtLaunchKernelGGL((grouped_gemm_bf16<BM, BN, WM, WN, BK, STAGES, MODE, false>), dim3(grid), block, 0,
+                          s, ev.start, ev.stop, 0, a);
   return hipGetLastError();
 }
 
 template <int BM, int BN, int WM, int WN, int BK, int STAGES>
-hipError_t launch_both(const GemmArgs& a, hipStream_t s) {
-  return a.mode == kGateUp ? launch_cfg<BM, BN, WM, WN, BK, STAGES, kGateUp>(a, s)
-                           : launch_cfg<BM, BN, WM, WN, BK, STAGES, kDown>(a, s);
+hipError_t launch_both(const GemmArgs& a, hipStream_t s, StageEvents ev) {
+  return a.mode == kGateUp ? launch_cfg<BM, BN, WM, WN, BK, STAGES, kGateUp>(a, s, ev)
+                           : launch_cfg<BM, BN, WM, WN, BK, STAGES, kDown>(a, s, ev);
 }
 
 // One 16-byte chunk (8 consecutive k of one row) per thread.
@@ -550,16 +555,24 @@ hipError_t launch_pack(const void* src, void* dst, int64_t count, int rows, int 
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
-  if (a.rows_total == 0) return hipSuccess;
+hipError_t record_stage(StageEvents ev, hipStream_t s) {
+  if (ev.start != nullptr) {
+    const hipError_t e = hipEventRecord(ev.start, s);
+    if (e != hipSuccess) return e;
+  }
+  return ev.stop != nullptr ? hipEventRecord(ev.stop, s) : hipSuccess;
+}
+
+hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s, StageEvents ev) {
+  if (a.rows_total == 0) return record_stage(ev, s);
   const int64_t mean_rows = a.rows_total / (a.offsets ? a.n_groups + a.n_extra : 1);
-  if (mean_rows >= 192) return launch_both<256, 256, 2, 4, 64, 2>(a, s);
-  if (mean_rows >= 64) return launch_both<128, 256, 2, 2, 64, 2>(a, s);
+  if (mean_rows >= 192) return launch_both<256, 256, 2, 4, 64, 2>(a, s, ev);
+  if (mean_rows >= 64) return launch_both<128, 256, 2, 2, 64, 2>(a, s, ev);
   // Few rows per group: the weights stream through and every workgroup's
   // time is its share of them.  Narrow down tiles (64 columns) split the
   // stream finer, so the last partial round of workgroups is short.
-  if (a.mode == kDown) return launch_cfg<32, 64, 1, 2, 64, 2, kDown>(a, s);
-  return launch_cfg<32, 256, 1, 4, 64, 2, kGateUp>(a, s);
+  if (a.mode == kDown) return launch_cfg<32, 64, 1, 2, 64, 2, kDown>(a, s, ev);
+  return launch_cfg<32, 256, 1, 4, 64, 2, kGateUp>(a, s, ev);
 }
 
 }  // namespace moe

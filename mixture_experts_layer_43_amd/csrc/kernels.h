@@ -124,7 +124,16 @@ struct GemmArgs {
   const void* Bx1;
   int64_t bx_group_stride, bx_bytes;
 };
-hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
+// Optional timing of one launch: the events take the kernel's own start and
+// end (hipExtLaunchKernel), so no marker packets sit between the kernels.  A
+// launch that has no work records both on the stream instead.
+struct StageEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+  bool any() const { return start != nullptr || stop != nullptr; }
+};
+hipError_t record_stage(StageEvents ev, hipStream_t s);
+hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s, StageEvents ev = {});
 hipError_t launch_gemm_f32(const GemmArgs& a, hipStream_t s);
 
 // ---- combine (combine.hip) ----
