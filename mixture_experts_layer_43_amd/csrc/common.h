@@ -11,6 +11,7 @@ constexpr int kWave = 64;  // CDNA wavefront width
 typedef uint16_t bf16_t;  // bfloat16 storage (bit pattern)
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t v) {

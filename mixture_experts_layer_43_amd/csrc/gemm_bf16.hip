@@ -39,6 +39,27 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 __device__ __forceinline__ lds_void_ptr lds_ptr(bf16_t* p) { return (lds_void_ptr)(p); }
 
 // silu(a) = a * sigmoid(a) with the hardware reciprocal (epilogue only).
+// 4x4 transpose across the lanes of each quad: lane i's m[j] becomes lane
+// j's m[i].  Two exchange rounds; in round b (1, 2) lane i takes register
+// j^b of lane i^b (DPP quad permutation) where bit b of i and j differ.
+__device__ __forceinline__ float dpp_quad_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_quad_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ void quad_transpose(float (&m)[4], int q4) {
+  float t[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) t[j] = dpp_quad_xor1(m[j ^ 1]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) m[j] = ((q4 ^ j) & 1) ? t[j] : m[j];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) t[j] = dpp_quad_xor2(m[j ^ 2]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) m[j] = ((q4 ^ j) & 2) ? t[j] : m[j];
+}
+
 __device__ __forceinline__ float silu_fast(float a) {
   return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a));
 }
@@ -444,58 +465,81 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
   }
 #undef MOE_K_LOOP
 
-  // ---- epilogue: the bf16 tile goes through LDS (the stage buffers are
-  //      free now) so that global stores are whole 16-byte chunks of rows.
-  //      D[row][col] of a 32x32 block sits in lane (col + 32*h), register v,
-  //      row = 8*(v/4) + 4*h + v%4.
-  //      In LDS, 16-byte chunk k of tile row r sits at chunk k ^ (r & 7), so
-  //      both the 2-byte writes and the 16-byte reads spread over the banks.
-  constexpr int NT = WM * WN * kWave;
-  static_assert(OUT_N % 64 == 0 && BM * OUT_N <= STAGES * SE, "C tile does not fit the stages");
-  __syncthreads();  // every wavefront is done reading the last stage
-  bf16_t* ct = smem;
-  auto cpos = [](int r, int c) { return r * OUT_N + ((((c >> 3) ^ (r & 7))) << 3) + (c & 7); };
-  const int col_in = lane & 31;
-  const int hrow = (lane >> 5) * 4;
-  if (MODE == kGateUp) {
-    constexpr int half = NB / 2;
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-      for (int j = 0; j < half; ++j) {
-        const int c = wn * (TN / 2) + j * 32 + col_in;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = wm * TM + i * 32 + 8 * (v >> 2) + hrow + (v & 3);
-          ct[cpos(r, c)] = f32_to_bf16(silu_fast(acc[i][j][v]) * acc[i][j + half][v]);
-        }
-      }
-  } else {
-    // ReLU FFN up projection: clamp at 0 (max with -inf leaves v as is).
-    const float lo = p.relu ? 0.0f : -INFINITY;
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int c = wn * TN + j * 32 + col_in;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = wm * TM + i * 32 + 8 * (v >> 2) + hrow + (v & 3);
-          ct[cpos(r, c)] = f32_to_bf16(fmaxf(acc[i][j][v], lo));
-        }
-      }
-  }
-  __syncthreads();
-  // Rows past the tile's end and columns past N (N is a multiple of 8) are
-  // not stored.
-  constexpr int CPR = OUT_N / 8;  // 16-byte chunks per tile row
+  // ---- epilogue.  D[row][col] of a 32x32 block sits in lane (col + 32*h),
+  //      register v, row = 8*(v/4) + 4*h + v%4.  Rows past the tile's end
+  //      and columns past N (a multiple of 8) are not stored.
+  constexpr int NBO = (MODE == kGateUp) ? NB / 2 : NB;   // output blocks per wavefront row
+  constexpr int TNO = (MODE == kGateUp) ? TN / 2 : TN;
+  // ReLU FFN up projection: clamp at 0 (max with -inf leaves v as is).
+  const float lo = (MODE == kDown && p.relu) ? 0.0f : -INFINITY;
   bf16_t* C = static_cast<bf16_t*>(p.C);
-  const int col0 = nt * OUT_N;
-  for (int idx = tid; idx < rows * CPR; idx += NT) {
-    const int r = idx / CPR, c8 = (idx % CPR) * 8;
-    if (col0 + c8 < p.N)
-      *reinterpret_cast<uint4*>(C + (row0 + r) * p.ldc + col0 + c8) =
-          *reinterpret_cast<const uint4*>(ct + cpos(r, c8));
+  const int hrow = (lane >> 5) * 4;
+  if constexpr (BM <= 32) {
+    // 32-row tiles (few rows per group, weight streaming): straight from
+    // the accumulators, with no LDS and no barrier.  A 4x4 transpose inside
+    // each quad of lanes turns the four rows of one column (registers
+    // 4g..4g+3) into four columns of one row, so every lane stores 8 bytes:
+    // row 8g + 4h + lane%4, columns 4 (col/4) .. +3.
+    const int q4 = lane & 3;
+    const int colq = (lane & 31) & ~3;
+    const int col0 = nt * OUT_N + wn * TNO;
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NBO; ++j)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          float m[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int v = 4 * g4 + u;
+            m[u] = (MODE == kGateUp) ? silu_fast(acc[i][j][v]) * acc[i][j + NBO][v]
+                                     : fmaxf(acc[i][j][v], lo);
+          }
+          quad_transpose(m, q4);
+          const int r = wm * TM + i * 32 + 8 * g4 + hrow + q4;
+          const int c = col0 + j * 32 + colq;
+          if (r < rows && c < p.N) {
+            uint2 o;
+            o.x = pack_bf16x2(m[0], m[1]);
+            o.y = pack_bf16x2(m[2], m[3]);
+            *reinterpret_cast<uint2*>(C + (row0 + r) * p.ldc + c) = o;
+          }
+        }
+  } else {
+    // Larger tiles: the bf16 tile goes through LDS (the stage buffers are
+    // free now) so that the global stores are whole 16-byte chunks of rows,
+    // a row of the tile per 16..32 lanes; they are non-temporal (the tile
+    // is not read again by this kernel).  In LDS, 16-byte chunk k of tile
+    // row r sits at chunk k ^ (r & 7), so both the 2-byte writes and the
+    // 16-byte reads spread over the banks.
+    constexpr int NT = WM * WN * kWave;
+    static_assert(OUT_N % 64 == 0 && BM * OUT_N <= STAGES * SE, "C tile does not fit the stages");
+    __syncthreads();  // every wavefront is done reading the last stage
+    bf16_t* ct = smem;
+    auto cpos = [](int r, int c) { return r * OUT_N + ((((c >> 3) ^ (r & 7))) << 3) + (c & 7); };
+    const int col_in = lane & 31;
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NBO; ++j) {
+        const int c = wn * TNO + j * 32 + col_in;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = wm * TM + i * 32 + 8 * (v >> 2) + hrow + (v & 3);
+          ct[cpos(r, c)] = f32_to_bf16((MODE == kGateUp) ? silu_fast(acc[i][j][v]) * acc[i][j + NBO][v]
+                                                         : fmaxf(acc[i][j][v], lo));
+        }
+      }
+    __syncthreads();
+    constexpr int CPR = OUT_N / 8;  // 16-byte chunks per tile row
+    const int col0 = nt * OUT_N;
+    for (int idx = tid; idx < rows * CPR; idx += NT) {
+      const int r = idx / CPR, c8 = (idx % CPR) * 8;
+      if (col0 + c8 < p.N)
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(ct + cpos(r, c8)),
+                                    reinterpret_cast<u32x4*>(C + (row0 + r) * p.ldc + col0 + c8));
+    }
   }
 #endif
 }
