@@ -519,16 +519,27 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
     bf16_t* ct = smem;
     auto cpos = [](int r, int c) { return r * OUT_N + ((((c >> 3) ^ (r & 7))) << 3) + (c & 7); };
     const int col_in = lane & 31;
+    // Rows r and r + 1 of a column (registers v, v + 1 for even v) are
+    // converted together and written as the two halves of one dword.
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
       for (int j = 0; j < NBO; ++j) {
         const int c = wn * TNO + j * 32 + col_in;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
+        for (int v = 0; v < 16; v += 2) {
           const int r = wm * TM + i * 32 + 8 * (v >> 2) + hrow + (v & 3);
-          ct[cpos(r, c)] = f32_to_bf16((MODE == kGateUp) ? silu_fast(acc[i][j][v]) * acc[i][j + NBO][v]
-                                                         : fmaxf(acc[i][j][v], lo));
+          float e0, e1;
+          if constexpr (MODE == kGateUp) {
+            e0 = silu_fast(acc[i][j][v]) * acc[i][j + NBO][v];
+            e1 = silu_fast(acc[i][j][v + 1]) * acc[i][j + NBO][v + 1];
+          } else {
+            e0 = fmaxf(acc[i][j][v], lo);
+            e1 = fmaxf(acc[i][j][v + 1], lo);
+          }
+          const uint32_t pr = pack_bf16x2(e0, e1);
+          ct[cpos(r, c)] = static_cast<bf16_t>(pr);
+          ct[cpos(r + 1, c)] = static_cast<bf16_t>(pr >> 16);
         }
       }
     __syncthreads();
