@@ -60,6 +60,11 @@ __device__ __forceinline__ void quad_transpose(float (&m)[4], int q4) {
   for (int j = 0; j < 4; ++j) m[j] = ((q4 ^ j) & 2) ? t[j] : m[j];
 }
 
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
+
 __device__ __forceinline__ float silu_fast(float a) {
   return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a));
 }
@@ -470,8 +475,8 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
   //      and columns past N (a multiple of 8) are not stored.
   constexpr int NBO = (MODE == kGateUp) ? NB / 2 : NB;   // output blocks per wavefront row
   constexpr int TNO = (MODE == kGateUp) ? TN / 2 : TN;
-  // ReLU FFN up projection: clamp at 0 (max with -inf leaves v as is).
-  const float lo = (MODE == kDown && p.relu) ? 0.0f : -INFINITY;
+  // The ReLU FFN's up projection (kDown with p.relu) clamps at 0; the two
+  // cases are separate instantiations of the store loops.
   bf16_t* C = static_cast<bf16_t*>(p.C);
   const int hrow = (lane >> 5) * 4;
   if constexpr (BM <= 32) {
@@ -483,6 +488,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
     const int q4 = lane & 3;
     const int colq = (lane & 31) & ~3;
     const int col0 = nt * OUT_N + wn * TNO;
+    auto store = [&](auto relu) {
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -493,8 +499,9 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int v = 4 * g4 + u;
-            m[u] = (MODE == kGateUp) ? silu_fast(acc[i][j][v]) * acc[i][j + NBO][v]
-                                     : fmaxf(acc[i][j][v], lo);
+            if constexpr (MODE == kGateUp) m[u] = silu_fast(acc[i][j][v]) * acc[i][j + NBO][v];
+            else if constexpr (decltype(relu)::value) m[u] = fmaxf(acc[i][j][v], 0.0f);
+            else m[u] = acc[i][j][v];
           }
           quad_transpose(m, q4);
           const int r = wm * TM + i * 32 + 8 * g4 + hrow + q4;
@@ -506,6 +513,11 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
             *reinterpret_cast<uint2*>(C + (row0 + r) * p.ldc + c) = o;
           }
         }
+    };
+    if (MODE == kDown && p.relu)
+      store(Flag<true>{});
+    else
+      store(Flag<false>{});
   } else {
     // Larger tiles: the bf16 tile goes through LDS (the stage buffers are
     // free now) so that the global stores are whole 16-byte chunks of rows,
@@ -520,28 +532,49 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
     auto cpos = [](int r, int c) { return r * OUT_N + ((((c >> 3) ^ (r & 7))) << 3) + (c & 7); };
     const int col_in = lane & 31;
     // Rows r and r + 1 of a column (registers v, v + 1 for even v) are
-    // converted together and written as the two halves of one dword.
+    // converted together and written as the two halves of one dword.  The
+    // byte address of an element is a lane part per (j, v % 4) - the
+    // swizzle sees only the row's low three bits, hrow + v % 4, as every
+    // wavefront's rows start at a multiple of 8 - plus a row offset known
+    // at compile time, which the LDS store takes as its immediate.
+    static_assert(TM % 8 == 0, "wavefront rows start at multiples of 8");
+    char* const cl = reinterpret_cast<char*>(smem) + (wm * TM + hrow) * (OUT_N * 2);
+    int colb[NBO][4];
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
+    for (int j = 0; j < NBO; ++j) {
+      const int c = wn * TNO + j * 32 + col_in;
 #pragma unroll
-      for (int j = 0; j < NBO; ++j) {
-        const int c = wn * TNO + j * 32 + col_in;
+      for (int u = 0; u < 4; ++u) colb[j][u] = ((((c >> 3) ^ (hrow + u)) << 3) + (c & 7)) * 2;
+    }
+    auto stage = [&](auto relu) {
 #pragma unroll
-        for (int v = 0; v < 16; v += 2) {
-          const int r = wm * TM + i * 32 + 8 * (v >> 2) + hrow + (v & 3);
-          float e0, e1;
-          if constexpr (MODE == kGateUp) {
-            e0 = silu_fast(acc[i][j][v]) * acc[i][j + NBO][v];
-            e1 = silu_fast(acc[i][j][v + 1]) * acc[i][j + NBO][v + 1];
-          } else {
-            e0 = fmaxf(acc[i][j][v], lo);
-            e1 = fmaxf(acc[i][j][v + 1], lo);
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NBO; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; v += 2) {
+            float e0, e1;
+            if constexpr (MODE == kGateUp) {
+              e0 = silu_fast(acc[i][j][v]) * acc[i][j + NBO][v];
+              e1 = silu_fast(acc[i][j][v + 1]) * acc[i][j + NBO][v + 1];
+            } else if constexpr (decltype(relu)::value) {
+              e0 = fmaxf(acc[i][j][v], 0.0f);
+              e1 = fmaxf(acc[i][j][v + 1], 0.0f);
+            } else {
+              e0 = acc[i][j][v];
+              e1 = acc[i][j][v + 1];
+            }
+            const uint32_t pr = pack_bf16x2(e0, e1);
+            const int ro = (i * 32 + 8 * (v >> 2) + (v & 3)) * (OUT_N * 2);
+            *reinterpret_cast<bf16_t*>(cl + ro + colb[j][v & 3]) = static_cast<bf16_t>(pr);
+            *reinterpret_cast<bf16_t*>(cl + ro + OUT_N * 2 + colb[j][(v & 3) + 1]) =
+                static_cast<bf16_t>(pr >> 16);
           }
-          const uint32_t pr = pack_bf16x2(e0, e1);
-          ct[cpos(r, c)] = static_cast<bf16_t>(pr);
-          ct[cpos(r + 1, c)] = static_cast<bf16_t>(pr >> 16);
-        }
-      }
+    };
+    if (MODE == kDown && p.relu)
+      stage(Flag<true>{});
+    else
+      stage(Flag<false>{});
     __syncthreads();
     constexpr int CPR = OUT_N / 8;  // 16-byte chunks per tile row
     const int col0 = nt * OUT_N;
