@@ -490,29 +490,29 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
     const int col0 = nt * OUT_N + wn * TNO;
     auto store = [&](auto relu) {
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
+      for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int j = 0; j < NBO; ++j)
+        for (int j = 0; j < NBO; ++j)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          float m[4];
+          for (int g4 = 0; g4 < 4; ++g4) {
+            float m[4];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int v = 4 * g4 + u;
-            if constexpr (MODE == kGateUp) m[u] = silu_fast(acc[i][j][v]) * acc[i][j + NBO][v];
-            else if constexpr (decltype(relu)::value) m[u] = fmaxf(acc[i][j][v], 0.0f);
-            else m[u] = acc[i][j][v];
+            for (int u = 0; u < 4; ++u) {
+              const int v = 4 * g4 + u;
+              if constexpr (MODE == kGateUp) m[u] = silu_fast(acc[i][j][v]) * acc[i][j + NBO][v];
+              else if constexpr (decltype(relu)::value) m[u] = fmaxf(acc[i][j][v], 0.0f);
+              else m[u] = acc[i][j][v];
+            }
+            quad_transpose(m, q4);
+            const int r = wm * TM + i * 32 + 8 * g4 + hrow + q4;
+            const int c = col0 + j * 32 + colq;
+            if (r < rows && c < p.N) {
+              uint2 o;
+              o.x = pack_bf16x2(m[0], m[1]);
+              o.y = pack_bf16x2(m[2], m[3]);
+              *reinterpret_cast<uint2*>(C + (row0 + r) * p.ldc + c) = o;
+            }
           }
-          quad_transpose(m, q4);
-          const int r = wm * TM + i * 32 + 8 * g4 + hrow + q4;
-          const int c = col0 + j * 32 + colq;
-          if (r < rows && c < p.N) {
-            uint2 o;
-            o.x = pack_bf16x2(m[0], m[1]);
-            o.y = pack_bf16x2(m[2], m[3]);
-            *reinterpret_cast<uint2*>(C + (row0 + r) * p.ldc + c) = o;
-          }
-        }
     };
     if (MODE == kDown && p.relu)
       store(Flag<true>{});
