@@ -13,6 +13,9 @@ namespace moe {
 
 namespace {
 
+// Up to this many tokens the combine spreads a token over several wavefronts.
+constexpr int kCombineSplitTokens = 1024;
+
 template <typename T>
 struct Vec16;  // 16 bytes of T as fp32 lanes
 template <>
@@ -48,11 +51,14 @@ struct Vec16<float> {
   }
 };
 
-// One wavefront per token; lane l owns the 16-byte column chunks
-// l, l + 64, ... (CPL of them per pass over 64*CPL chunks).  The rows to sum are the K' routed rows
-// (weight topk_w), then the shared-expert rows and the residual (weight 1),
-// taken JG at a time with all their loads in flight before any is used.
-template <typename E, int CPL>
+// SPLIT wavefronts per token (1, or up to 4 for small batches so that more
+// loads are in flight); wavefront p of a token owns the column chunks
+// 64 p + l, 64 (p + SPLIT) + l, ... (CPL of them per pass), lane l.  The
+// token's K' row indices and gate values are loaded once, by lanes 0..K'-1,
+// and broadcast.  The rows to sum are the K' routed rows (weight topk_w),
+// then the shared-expert rows and the residual (weight 1), taken JG at a time
+// with all their loads in flight before any is used.
+template <typename E, int CPL, int SPLIT>
 __global__ __launch_bounds__(256) void combine_kernel(
     const char* __restrict__ y_perm, const int32_t* __restrict__ slot_row,
     const float* __restrict__ topk_w, const char* __restrict__ y_shared,
@@ -60,84 +66,95 @@ __global__ __launch_bounds__(256) void combine_kernel(
     char* __restrict__ y, int T, int chunks, int K) {
   using V = Vec16<E>;
   constexpr int N = V::N;
-  constexpr int JG = CPL <= 4 ? 4 : 2;
+  constexpr int JG = CPL == 1 ? 8 : CPL <= 4 ? 4 : 2;
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * (256 / kWave) + threadIdx.x / kWave;
+  const int64_t gw = static_cast<int64_t>(blockIdx.x) * (256 / kWave) + threadIdx.x / kWave;
+  const int64_t t = gw / SPLIT;
+  const int part = static_cast<int>(gw % SPLIT);
   if (t >= T) return;
   const int64_t row_bytes = static_cast<int64_t>(chunks) * 16;
   const int nrows = K + shared_blocks + (residual != nullptr ? 1 : 0);
-  for (int cb = 0; cb < chunks; cb += kWave * CPL) {
-  float acc[CPL][N];
+  int my_sr = 0;
+  float my_w = 0.0f;
+  if (lane < K) {
+    my_sr = slot_row[t * K + lane];
+    my_w = topk_w[t * K + lane];
+  }
+  for (int cb = part * kWave * CPL; cb < chunks; cb += SPLIT * kWave * CPL) {
+    float acc[CPL][N];
 #pragma unroll
-  for (int i = 0; i < CPL; ++i)
+    for (int i = 0; i < CPL; ++i)
 #pragma unroll
-    for (int n = 0; n < N; ++n) acc[i][n] = 0.0f;
-  for (int j0 = 0; j0 < nrows; j0 += JG) {
-    // Branch-free issue (so all loads of the group are in flight together):
-    // rows past the end re-read the last row, columns past the end re-read
-    // the last chunk; neither is used.
-    float v[JG][CPL][N];
-    bool dropped[JG];
+      for (int n = 0; n < N; ++n) acc[i][n] = 0.0f;
+    for (int j0 = 0; j0 < nrows; j0 += JG) {
+      // Branch-free issue (so all loads of the group are in flight together):
+      // rows past the end re-read the last row, columns past the end re-read
+      // the last chunk; neither is used.
+      float v[JG][CPL][N];
+      bool dropped[JG];
 #pragma unroll
-    for (int jj = 0; jj < JG; ++jj) {
-      const int j = min(j0 + jj, nrows - 1);
-      // slot_row -1: an assignment dropped by the expert capacity (gate 0);
-      // row 0 is read in its place and not used.
-      const int sr = slot_row[t * K + min(j, K - 1)];
-      dropped[jj] = j < K && sr < 0;
-      const char* routed = y_perm + static_cast<int64_t>(max(sr, 0)) * row_bytes;
-      const char* shared = (shared_blocks > 0 ? y_shared : y_perm) +
-                           max(j - K, 0) * shared_stride_bytes + t * row_bytes;
-      const char* res = (residual != nullptr ? residual : y_perm) + t * row_bytes;
-      const char* row = j < K ? routed : (j < K + shared_blocks ? shared : res);
+      for (int jj = 0; jj < JG; ++jj) {
+        const int j = min(j0 + jj, nrows - 1);
+        // slot_row -1: an assignment dropped by the expert capacity (gate 0);
+        // row 0 is read in its place and not used.
+        const int sr = __shfl(my_sr, min(j, K - 1), kWave);
+        dropped[jj] = j < K && sr < 0;
+        const char* routed = y_perm + static_cast<int64_t>(max(sr, 0)) * row_bytes;
+        const char* shared = (shared_blocks > 0 ? y_shared : y_perm) +
+                             max(j - K, 0) * shared_stride_bytes + t * row_bytes;
+        const char* res = (residual != nullptr ? residual : y_perm) + t * row_bytes;
+        const char* row = j < K ? routed : (j < K + shared_blocks ? shared : res);
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const int c = min(cb + lane + kWave * i, chunks - 1);
-        V::load(row + static_cast<int64_t>(c) * 16, v[jj][i]);
+        for (int i = 0; i < CPL; ++i) {
+          const int c = min(cb + lane + kWave * i, chunks - 1);
+          V::load(row + static_cast<int64_t>(c) * 16, v[jj][i]);
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < JG; ++jj) {
+        const int j = j0 + jj;
+        if (j >= nrows) break;
+        if (dropped[jj]) continue;  // uniform: one token per wavefront
+        const float w = j < K ? __shfl(my_w, j, kWave) : 1.0f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i)
+#pragma unroll
+          for (int n = 0; n < N; ++n) acc[i][n] = fmaf(w, v[jj][i][n], acc[i][n]);
       }
     }
 #pragma unroll
-    for (int jj = 0; jj < JG; ++jj) {
-      const int j = j0 + jj;
-      if (j >= nrows) break;
-      if (dropped[jj]) continue;  // uniform: one token per wavefront
-      const float w = j < K ? topk_w[t * K + j] : 1.0f;
-#pragma unroll
-      for (int i = 0; i < CPL; ++i)
-#pragma unroll
-        for (int n = 0; n < N; ++n) acc[i][n] = fmaf(w, v[jj][i][n], acc[i][n]);
+    for (int i = 0; i < CPL; ++i) {
+      const int c = cb + lane + kWave * i;
+      if (c < chunks) V::store(y + t * row_bytes + static_cast<int64_t>(c) * 16, acc[i]);
     }
-  }
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-    const int c = cb + lane + kWave * i;
-    if (c < chunks) V::store(y + t * row_bytes + static_cast<int64_t>(c) * 16, acc[i]);
-  }
   }
 }
 
 template <typename E>
 hipError_t launch_combine_t(const CombineArgs& a, int chunks, hipStream_t s) {
-  const int grid = (a.T + 3) / 4;
   const int blocks = a.y_shared ? a.shared_blocks : 0;
   const int64_t stride = a.shared_stride * static_cast<int64_t>(sizeof(E));
   const char* yp = static_cast<const char*>(a.y_perm);
   const char* ys = static_cast<const char*>(a.y_shared);
   const char* res = static_cast<const char*>(a.residual);
   char* y = static_cast<char*>(a.y);
+#define MOE_COMBINE(CPL, SPLIT)                                                                    \
+  hipLaunchKernelGGL((combine_kernel<E, CPL, SPLIT>),                                            \
+                     dim3(static_cast<unsigned>((static_cast<int64_t>(a.T) * SPLIT + 3) / 4)),    \
+                     dim3(256), 0, s, yp, a.slot_row, a.topk_w, ys, blocks, stride, res, y, a.T, \
+                     chunks, a.top_k)
+  // Small batches: a token's rows over several wavefronts, one chunk per
+  // lane per row, all rows of the token in flight at once.
+  const int split = a.T <= kCombineSplitTokens ? min(4, max(1, chunks / kWave)) : 1;
   const int cpl = (chunks + kWave - 1) / kWave;
-  if (cpl <= 1)
-    hipLaunchKernelGGL((combine_kernel<E, 1>), dim3(grid), dim3(256), 0, s, yp, a.slot_row, a.topk_w,
-                       ys, blocks, stride, res, y, a.T, chunks, a.top_k);
-  else if (cpl <= 2)
-    hipLaunchKernelGGL((combine_kernel<E, 2>), dim3(grid), dim3(256), 0, s, yp, a.slot_row, a.topk_w,
-                       ys, blocks, stride, res, y, a.T, chunks, a.top_k);
-  else if (cpl <= 4)
-    hipLaunchKernelGGL((combine_kernel<E, 4>), dim3(grid), dim3(256), 0, s, yp, a.slot_row, a.topk_w,
-                       ys, blocks, stride, res, y, a.T, chunks, a.top_k);
-  else  // rows longer than 8 KB take several passes of 512 chunks
-    hipLaunchKernelGGL((combine_kernel<E, 8>), dim3(grid), dim3(256), 0, s, yp, a.slot_row, a.topk_w,
-                       ys, blocks, stride, res, y, a.T, chunks, a.top_k);
+  if (split == 4) MOE_COMBINE(1, 4);
+  else if (split == 3) MOE_COMBINE(1, 3);
+  else if (split == 2) MOE_COMBINE(1, 2);
+  else if (cpl <= 1) MOE_COMBINE(1, 1);
+  else if (cpl <= 2) MOE_COMBINE(2, 1);
+  else if (cpl <= 4) MOE_COMBINE(4, 1);
+  else MOE_COMBINE(8, 1);  // rows longer than 8 KB take several passes of 512 chunks
+#undef MOE_COMBINE
   return hipGetLastError();
 }
 
