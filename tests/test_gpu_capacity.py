@@ -93,11 +93,14 @@ def test_gshard_zipf_full_size_with_capacity(factor):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("S,C", [(0, 3), (4, 3), (50, 1)])
-def test_forced_overflow(S, C):
+@pytest.mark.parametrize("base,S,C", [("mid-ragged", 0, 3), ("mid-ragged", 4, 3), ("mid-ragged", 50, 1),
+                                      ("16b-decode", 16, 5)])
+def test_forced_overflow(base, S, C):
     """Every token chooses experts 5 and 11; beyond the first C tokens of a
-    group, tokens overflow and y = shared experts + residual."""
-    cfg = MID["mid-ragged"].with_(tokens=300, top_k=2, capacity=C, group_size=S, seed=700 + S)
+    group, tokens overflow and y = shared experts + residual.  The decode
+    shape's combine spreads a token over four wavefronts."""
+    T = 300 if base == "mid-ragged" else 128
+    cfg = cfg_of(base).with_(tokens=T, top_k=2, capacity=C, group_size=S, seed=700 + S)
     inp = prepare(cfg)
     bias = np.zeros(cfg.n_routed, np.float32)
     bias[[5, 11]] = 40.0

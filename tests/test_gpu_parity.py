@@ -155,7 +155,7 @@ def test_shared_ffn_alone(name):
     check_y(host(y), want, cfg.dtype, "y_shared")
 
 
-@pytest.mark.parametrize("name", ["tiny-f32", "mid-ragged"])
+@pytest.mark.parametrize("name", ["tiny-f32", "mid-ragged", "16b-decode"])
 def test_combine_alone(name):
     """Combine fed with oracle expert rows (rounded to the layer dtype)."""
     cfg, inp, ref = case(name)
@@ -200,9 +200,12 @@ def test_forward_full_size_sampled(name):
     torch.cuda.empty_cache()
 
 
-def test_residual_is_added():
-    cfg, inp, _ = case("mid-ragged")
-    announce("residual mid-ragged")
+@pytest.mark.parametrize("name", ["mid-ragged", "16b-decode"])
+def test_residual_is_added(name):
+    """Also at the decode shape, whose combine spreads a token over four
+    wavefronts."""
+    cfg, inp, _ = case(name)
+    announce(f"residual {name}")
     ref = oracle.forward(cfg, inp, residual=True)
     d = upload(inp)
     f = run_forward(cfg, d, residual=d["x"])
