@@ -11,14 +11,18 @@ constexpr int kDispatchMaxK = 16;
 constexpr int kDispatchMaxExperts = 256;
 
 // Stable counting sort of the T*K assignments of topk_idx (T <= kSmallTokens)
-// by expert, one thread per token: ballots give per-wave counts and in-wave
-// ranks (only the wavefronts that hold tokens take part); the scan runs over
-// experts in LDS; a row is the first row of (wave, expert) - offsets[e] plus
-// the rows of e in earlier waves - plus the rank in the wave, i.e.
-// ascending token order.  Every thread of the workgroup must call it.
+// by expert, one thread per token.  Each wavefront that holds tokens keeps a
+// 64-bit mask per expert of its lanes (tokens) that chose it: it clears its
+// own masks, then every lane ORs its bit into the masks of its K experts
+// (LDS operations of one wavefront run in order, so no barrier is needed in
+// between).  Popcounts of the masks give per-wave counts and in-wave ranks;
+// the scan runs over experts in LDS; a row is the first row of (wave,
+// expert) - offsets[e] plus the rows of e in earlier waves - plus the rank
+// in the wave, i.e. ascending token order.  Every thread of the workgroup
+// must call it.
 struct SmallDispatchLds {
   uint64_t masks[kSmallTokens / kWave][kDispatchMaxExperts];
-  int cnt[kSmallTokens / kWave][kDispatchMaxExperts];   // then: first row of (wave, expert)
+  int cnt[kSmallTokens / kWave][kDispatchMaxExperts];   // first row of (wave, expert)
   int offs[kDispatchMaxExperts + 1];
 };
 
@@ -33,38 +37,23 @@ __device__ __forceinline__ void small_dispatch(const int32_t* __restrict__ idx, 
   const int t = threadIdx.x;
   const bool valid = t < T;
   int ids[kDispatchMaxK];
-  uint64_t bits0 = 0, bits1 = 0, bits2 = 0, bits3 = 0;
 #pragma unroll
   for (int j = 0; j < kDispatchMaxK; ++j) {
     ids[j] = -1;
-    if (j < K && valid) {
-      const int e = idx[static_cast<int64_t>(t) * K + j];
-      ids[j] = e;
-      const uint64_t b = 1ull << (e & 63);
-      const int w = e >> 6;
-      bits0 |= (w == 0) ? b : 0ull;
-      bits1 |= (w == 1) ? b : 0ull;
-      bits2 |= (w == 2) ? b : 0ull;
-      bits3 |= (w == 3) ? b : 0ull;
-    }
+    if (j < K && valid) ids[j] = idx[static_cast<int64_t>(t) * K + j];
   }
   if (wave < NWV) {
-    for (int e = 0; e < Nr; ++e) {
-      const int w = e >> 6;
-      const uint64_t bits = (w == 0) ? bits0 : (w == 1) ? bits1 : (w == 2) ? bits2 : bits3;
-      const uint64_t m = __ballot((bits >> (e & 63)) & 1ull);
-      if (lane == 0) {
-        sh.masks[wave][e] = m;
-        sh.cnt[wave][e] = __popcll(m);
-      }
-    }
+    for (int e = lane; e < Nr; e += kWave) sh.masks[wave][e] = 0ull;
+#pragma unroll
+    for (int j = 0; j < kDispatchMaxK; ++j)
+      if (j < K && valid) atomicOr(&sh.masks[wave][ids[j]], 1ull << lane);
   }
   __syncthreads();
   // Per-expert totals in parallel, then an exclusive scan over the experts
   // in wavefront 0 (four experts per lane, shuffle prefix sums).
   if (threadIdx.x < Nr) {
     int c = 0;
-    for (int w = 0; w < NWV; ++w) c += sh.cnt[w][threadIdx.x];
+    for (int w = 0; w < NWV; ++w) c += __popcll(sh.masks[w][threadIdx.x]);
     sh.offs[threadIdx.x + 1] = c;
   }
   __syncthreads();
@@ -97,13 +86,12 @@ __device__ __forceinline__ void small_dispatch(const int32_t* __restrict__ idx, 
     if (e < Nr) counts[e] = sh.offs[e + 1] - sh.offs[e];
   }
   // First row of each (wavefront, expert): the expert's offset plus the
-  // rows of the wavefronts before (cnt is overwritten in place).
+  // rows of the wavefronts before.
   if (threadIdx.x < Nr) {
     int run = sh.offs[threadIdx.x];
     for (int w = 0; w < NWV; ++w) {
-      const int c = sh.cnt[w][threadIdx.x];
       sh.cnt[w][threadIdx.x] = run;
-      run += c;
+      run += __popcll(sh.masks[w][threadIdx.x]);
     }
   }
   __syncthreads();
