@@ -5,10 +5,11 @@
 //
 // Three launches (one for small batches without the row copy), no host
 // synchronisation:
-//   count   one thread per token, 256 tokens per block.  Per wave, one ballot
-//           per expert gives the set of lanes that chose it; its popcount is
-//           the wave's count, and popcount(mask & lanes-below) is the stable
-//           rank of a token inside the wave.  Block totals go to block_counts.
+//   count   one thread per token, 256 tokens per block.  Per wave, a 64-bit
+//           mask per expert of the lanes that chose it (built with LDS
+//           atomic ORs); its popcount is the wave's count, and
+//           popcount(mask & lanes-below) is the stable rank of a token inside
+//           the wave.  Block totals go to block_counts.
 //   scan    one block: per-expert totals over blocks, exclusive scan over
 //           experts (offsets), and the first row of every (block, expert).
 //   scatter row = block_base[block, e] + local rank: writes row_token,
@@ -29,42 +30,29 @@ __global__ __launch_bounds__(kCountBlock) void count_kernel(
     const int32_t* __restrict__ idx, int T, int K, int Nr, int32_t* __restrict__ block_counts,
     int32_t* __restrict__ local_rank) {
   __shared__ uint64_t masks[kCountBlock / kWave][kMaxExperts];
-  __shared__ int cnt[kCountBlock / kWave][kMaxExperts];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kCountBlock + threadIdx.x;
   const bool valid = t < T;
 
+  // Each wavefront clears its 64-bit mask per expert, then every lane ORs
+  // its bit into the masks of its K experts (a wavefront's LDS operations
+  // run in order, so no barrier in between).
   int ids[kMaxK];
-  uint64_t bits0 = 0, bits1 = 0, bits2 = 0, bits3 = 0;
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
     ids[j] = -1;
-    if (j < K && valid) {
-      const int e = idx[t * K + j];
-      ids[j] = e;
-      const uint64_t b = 1ull << (e & 63);
-      const int w = e >> 6;
-      bits0 |= (w == 0) ? b : 0ull;
-      bits1 |= (w == 1) ? b : 0ull;
-      bits2 |= (w == 2) ? b : 0ull;
-      bits3 |= (w == 3) ? b : 0ull;
-    }
+    if (j < K && valid) ids[j] = idx[t * K + j];
   }
-  for (int e = 0; e < Nr; ++e) {
-    const int w = e >> 6;
-    const uint64_t bits = (w == 0) ? bits0 : (w == 1) ? bits1 : (w == 2) ? bits2 : bits3;
-    const uint64_t m = __ballot((bits >> (e & 63)) & 1ull);
-    if (lane == 0) {
-      masks[wave][e] = m;
-      cnt[wave][e] = __popcll(m);
-    }
-  }
+  for (int e = lane; e < Nr; e += kWave) masks[wave][e] = 0ull;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j)
+    if (j < K && valid) atomicOr(&masks[wave][ids[j]], 1ull << lane);
   __syncthreads();
   for (int e = threadIdx.x; e < Nr; e += kCountBlock) {
     int s = 0;
 #pragma unroll
-    for (int w = 0; w < kCountBlock / kWave; ++w) s += cnt[w][e];
+    for (int w = 0; w < kCountBlock / kWave; ++w) s += __popcll(masks[w][e]);
     block_counts[static_cast<int64_t>(blockIdx.x) * Nr + e] = s;
   }
   if (!valid) return;
@@ -74,7 +62,7 @@ __global__ __launch_bounds__(kCountBlock) void count_kernel(
     if (j < K) {
       const int e = ids[j];
       int r = __popcll(masks[wave][e] & below);
-      for (int w = 0; w < wave; ++w) r += cnt[w][e];
+      for (int w = 0; w < wave; ++w) r += __popcll(masks[w][e]);
       local_rank[t * K + j] = r;
     }
   }
