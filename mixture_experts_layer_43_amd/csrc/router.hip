@@ -512,22 +512,28 @@ __global__ __launch_bounds__(kRW * kWave) void router_mfma_kernel(
   if (rs + 2 <= s1) { router_round<2, RD, MBLK, NBLK>(acc, xp, wp, ev, rs); rs += 2; }
   if (rs + 1 <= s1) router_round<1, RD, MBLK, NBLK>(acc, xp, wp, ev, rs);
 
+  // Sum of the wavefronts' partial tiles in wavefront order: each writes its
+  // tile to its own LDS slot, then every thread adds its elements' kRW
+  // values in order (the same additions as accumulating wave by wave).
   // D[row][col] of a 32x32 block: lane (col + 32*h), register v, row 8*(v/4) + 4*h + v%4.
-  for (int w = 0; w < kRW; ++w) {
-    if (wave == w) {
+  __shared__ __align__(16) float slot[kRW][TB * NPAD];
 #pragma unroll
-      for (int mb = 0; mb < MBLK; ++mb)
+  for (int mb = 0; mb < MBLK; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NBLK; ++nb)
+    for (int nb = 0; nb < NBLK; ++nb)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int r = mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            const int c = nb * 32 + lr;
-            lg[r][c] = (w == 0) ? acc[mb][nb][v] : lg[r][c] + acc[mb][nb][v];
-          }
-    }
-    __syncthreads();
+      for (int v = 0; v < 16; ++v) {
+        const int r = mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        slot[wave][r * NPAD + nb * 32 + lr] = acc[mb][nb][v];
+      }
+  __syncthreads();
+  for (int i = threadIdx.x; i < TB * NPAD; i += kRW * kWave) {
+    float sum = slot[0][i];
+#pragma unroll
+    for (int w = 1; w < kRW; ++w) sum += slot[w][i];
+    lg[i / NPAD][i % NPAD] = sum;
   }
+  __syncthreads();
 
   if (KS > 1) {
     for (int i = threadIdx.x; i < TB * NPAD; i += kRW * kWave) {
