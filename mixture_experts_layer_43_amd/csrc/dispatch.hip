@@ -25,6 +25,7 @@ namespace {
 
 constexpr int kMaxK = 16;
 constexpr int kMaxExperts = 256;
+static_assert(kMaxExperts <= 4 * kWave, "the expert scans take four experts per lane");
 
 __global__ __launch_bounds__(kCountBlock) void count_kernel(
     const int32_t* __restrict__ idx, int T, int K, int Nr, int32_t* __restrict__ block_counts,
@@ -98,13 +99,31 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     tot[e] = run;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int i = 0; i < Nr; ++i) {
-      offs[i] = run;
-      run += tot[i];
+  // Exclusive scan over the experts in wavefront 0: four experts per lane,
+  // shuffle prefix sums.
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    int v[4], sum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int ei = lane * 4 + q;
+      v[q] = ei < Nr ? tot[ei] : 0;
+      sum += v[q];
     }
-    offs[Nr] = run;
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int u = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += u;
+    }
+    int run = incl - sum;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int ei = lane * 4 + q;
+      if (ei < Nr) offs[ei] = run;
+      run += v[q];
+    }
+    if (lane == kWave - 1) offs[Nr] = incl;
   }
   __syncthreads();
   if (threadIdx.x < Nr) {
