@@ -14,6 +14,12 @@ to its launch on the launch stream (the kernel's own start and end); the
 per-stage breakdown comes from a few further steps with every marker set,
 outside the timed region.
 
+Warm-up runs at least --warmup steps and keeps going until WARMUP_MIN_S of
+back-to-back steps have passed: from an idle GPU the step time falls for
+the first 25-50 ms of sustained load (2b-shaped layer 0.67 -> 0.55 ms, 16B
+2.73 -> 2.30 ms, measured step by step) as the clocks come up, and a few
+steps do not cover that.  The JSON line gives the count actually run.
+
 Prints one JSON line.  `roofline` is for the dominant kernel, the gate/up
 grouped GEMM, whose launch does 4*R*d*I FLOPs (R = T*K' routed rows, plus
 K_s*T rows when the shared experts of the routed width ride in the same
@@ -41,6 +47,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+WARMUP_MIN_S = 0.2            # least back-to-back warm-up before timing
 
 # HBM bytes per launch of the routed gate/up kernel, by (layer, weight layout),
 # from rocprofv3 FETCH_SIZE (x2) and WRITE_SIZE (x1) in KiB, the factors taken
@@ -141,9 +148,12 @@ def main():
     fwd = ops.Forward(lay, cfg.tokens, dev)
     fwd.check(*call_args, None)
 
-    for _ in range(args.warmup):
-        fwd(*call_args, checked=True)
-    torch.cuda.synchronize()
+    warmup_run, t_w = 0, time.perf_counter()
+    while warmup_run < args.warmup or time.perf_counter() - t_w < WARMUP_MIN_S:
+        for _ in range(max(1, args.warmup)):
+            fwd(*call_args, checked=True)
+        warmup_run += max(1, args.warmup)
+        torch.cuda.synchronize()
 
     hip = hip_runtime()
     nev = 2 * _lib.MOE_NUM_STAGES
@@ -334,6 +344,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_run": warmup_run,
         "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
