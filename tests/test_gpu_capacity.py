@@ -37,7 +37,7 @@ def check_dispatch(got, ref, x=None, inp=None):
 PERMUTE = [("mid-ragged", 1.0, 0), ("mid-ragged", 0.5, 100), ("mid-ragged", 1.25, 256),
            ("mid-smallm", 1.0, 0), ("mid-smallm", 0.8, 37), ("mid-many-tokens", 1.0, 333),
            ("mid-gshard", 1.0, 0), ("mid-many-experts", 1.5, 64), ("16b-decode", 1.0, 0),
-           ("16b-decode", 2.0, 16)]
+           ("16b-decode", 2.0, 16), ("mid-max-experts", 1.0, 64)]
 
 
 @pytest.mark.parametrize("name,factor,S", PERMUTE, ids=[f"{n}-f{f}-S{S}" for n, f, S in PERMUTE])
@@ -59,7 +59,7 @@ def test_permute_with_capacity_is_bit_exact(name, factor, S, copy):
 
 FORWARD = [("mid-ragged", 1.0, 0), ("mid-ragged", 0.7, 128), ("mid-smallm", 1.0, 50),
            ("mid-gshard", 1.0, 0), ("mid-gshard", 1.25, 200), ("mid-f32", 1.0, 0),
-           ("mid-medm", 1.0, 64), ("16b-decode", 1.0, 0)]
+           ("mid-medm", 1.0, 64), ("16b-decode", 1.0, 0), ("mid-max-experts", 1.5, 100)]
 
 
 @pytest.mark.parametrize("name,factor,S", FORWARD, ids=[f"{n}-f{f}-S{S}" for n, f, S in FORWARD])

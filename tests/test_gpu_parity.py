@@ -35,6 +35,9 @@ MID = {
                               top_k=16, d_ff=64, d_ff_shared=64, seed=106),
     "mid-many-experts": LayerConfig(name="mid-many-experts", tokens=300, d_model=128, n_routed=200,
                                     n_shared=0, top_k=8, d_ff=64, d_ff_shared=64, seed=107),
+    # The largest expert count and top-K' the layer accepts (256, 16).
+    "mid-max-experts": LayerConfig(name="mid-max-experts", tokens=300, d_model=128, n_routed=256,
+                                   n_shared=1, top_k=16, d_ff=64, d_ff_shared=64, seed=109),
     # More tokens than the single-workgroup dispatch takes (1024).
     "mid-many-tokens": LayerConfig(name="mid-many-tokens", tokens=2500, d_model=64, n_routed=24,
                                    n_shared=1, top_k=5, d_ff=64, d_ff_shared=64, seed=108),
@@ -82,7 +85,7 @@ def check_routing(f, ref):
 
 
 @pytest.mark.parametrize("name", ["tiny-f32", "mid-ragged", "mid-gshard", "mid-wide-k",
-                                  "mid-many-experts", "mid-smallm", "2b"])
+                                  "mid-many-experts", "mid-max-experts", "mid-smallm", "2b"])
 def test_route_alone(name):
     cfg, inp, ref = case(name)
     announce(f"route {name}")
@@ -93,7 +96,7 @@ def test_route_alone(name):
 
 
 @pytest.mark.parametrize("name", ["tiny-f32", "mid-ragged", "mid-smallm", "mid-wide-k", "16b-decode",
-                                  "mid-many-tokens"])
+                                  "mid-many-tokens", "mid-max-experts"])
 def test_permute_alone_is_bit_exact(name):
     cfg, inp, ref = case(name)
     announce(f"permute {name}")
