@@ -210,6 +210,10 @@ int moe_route_stats(const moe_layer* layer, int64_t T, const void* x, const floa
 
 /* Dispatch: stable counting sort of the T*K' (token, expert) assignments by
  * expert (the per-expert token lists that let only chosen experts run).
+ * Passage: MoE-survey blog page, section 2 (sparsely-gated MoE): y is
+ * sum_i G(x)_i E_i(x) and E_i is not evaluated where G(x)_i is zero, so each
+ * expert needs the list of tokens whose gate for it is non-zero; the
+ * DeepSeekMoE page, section 3.2, eq. 10, fixes K' such experts per token.
  *   topk_idx [T, K'] with 0 <= id < N_r and distinct ids per token (other
  *   input is undefined behaviour), x [T, d] (dtype)
  *   -> counts [N_r], offsets [N_r + 1] (exclusive scan, offsets[N_r] = P),
@@ -249,6 +253,10 @@ int moe_combine(const moe_layer* layer, int64_t T, const void* y_perm, const int
                 void* stream);
 
 /* The whole layer: route, dispatch, routed and shared experts, combine.
+ * Passage: DeepSeekMoE page, section 3.2, eq. 9-11 (h_t = sum of the K_s
+ * shared FFNs + sum of g_{i,t} FFN_i(u_t) over the routed experts, with
+ * the gates of eq. 10-11); MoE-survey blog page, section 2 (y = sum_i
+ * G(x)_i E_i(x), only experts with non-zero gate evaluated).
  * The gather of x rows is fused into the routed gate/up GEMM, so no x_perm
  * is materialised.  When I_s == I the K_s shared experts run inside the
  * routed gate/up and down launches as K_s extra groups of all T tokens,

@@ -7,7 +7,8 @@ the two share nothing except the seeded inputs from `synth`.
 
 Every function is pinned by tests/test_oracle_pins.py (the layer) and
 tests/test_oracle_stats_pins.py (routing statistics) and
-tests/test_oracle_capacity_pins.py (capacity-limited dispatch) against closed forms,
+tests/test_oracle_capacity_pins.py (capacity-limited dispatch) and
+tests/test_oracle_decode_pins.py (bf16 storage decoding) against closed forms,
 special cases and a pure-Python brute force (see tests/_brute.py).
 """
 from .moe import (  # noqa: F401

@@ -61,8 +61,8 @@ CASES = {
 @pytest.mark.parametrize("name,kw", [("16b-decode", {}), ("unfolded-shared", {}), ("folded-shared", {}),
                                      ("folded-shared", dict(ffn="relu")),
                                      ("unfolded-shared", dict(capacity=120, group_size=256)),
-                                     ("2b", {})],
-                         ids=["decode", "unfolded", "folded", "relu", "capacity", "2b"])
+                                     ("2b", {}), ("16b", {})],
+                         ids=["decode", "unfolded", "folded", "relu", "capacity", "2b", "16b"])
 def test_packed_forward_equals_row_major(name, kw):
     cfg = (CASES[name] if name in CASES else cfg_of(name)).with_(**kw)
     announce(f"packed forward {name} {kw}")
@@ -80,6 +80,8 @@ def test_packed_forward_equals_row_major(name, kw):
     torch.cuda.synchronize()
     assert torch.equal(f.topk_idx, idx0)
     assert torch.equal(f.y, y0)
+    del f, dp
+    torch.cuda.empty_cache()
     if cfg.tokens <= 1000:
         check_y(host(f.y), oracle.forward(cfg, inp)["y"], cfg.dtype)
 
