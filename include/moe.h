@@ -17,9 +17,11 @@
  * Conventions shared by every entry point
  *   - Tensors are dense and row-major.  Every data pointer is a device
  *     pointer owned by the caller; the library never allocates, frees or
- *     synchronises, and holds no global state besides the thread-local last
- *     HIP error.  Scratch memory comes only from the caller's `ws` buffer,
- *     sized by moe_workspace_size().
+ *     synchronises.  Scratch memory comes from the caller's `ws` buffer,
+ *     sized by moe_workspace_size(), except in moe_forward_noalloc, which
+ *     takes it from a static device array (its global state, with the
+ *     per-device address of that array and the thread-local last HIP
+ *     error).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Every call only enqueues work on it and returns.
  *   - Weights are [out_features, in_features] (in_features contiguous):
@@ -52,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
   MOE_OK = 0,
@@ -61,7 +63,9 @@ typedef enum {
                                        weight_layout                                             */
   MOE_ERR_UNSUPPORTED = 2,          /* shape/alignment outside the supported set above         */
   MOE_ERR_WORKSPACE_TOO_SMALL = 3,  /* ws_bytes below moe_workspace_size()                      */
-  MOE_ERR_HIP = 4                   /* a HIP launch or query failed                              */
+  MOE_ERR_HIP = 4,                  /* a HIP launch or query failed                              */
+  MOE_ERR_SCRATCH_TOO_SMALL = 5     /* moe_forward_noalloc: the layer at T needs more scratch than
+                                       MOE_STATIC_SCRATCH_BYTES                                  */
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
@@ -304,6 +308,34 @@ int moe_forward_timed(const moe_layer* layer, int64_t T, const void* x, const fl
                       const void* ws_down, const void* residual, void* y, int32_t* topk_idx,
                       float* topk_w, int32_t* counts, int32_t* offsets, void* ws,
                       size_t ws_bytes, void* stream, void* const* events);
+
+/* Bytes of the static device scratch array of moe_forward_noalloc. */
+#define MOE_STATIC_SCRATCH_BYTES (64 * 1024 * 1024)
+
+/* moe_forward for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * launches and results as moe_forward, bit for bit, with the scratch taken
+ * from a static device array of MOE_STATIC_SCRATCH_BYTES instead of a `ws`
+ * argument.  The caller still passes inputs and outputs.  Each GPU the
+ * library runs this on holds its own array from the first call on that GPU
+ * (which also looks up the array's address, with the current device) until
+ * the process ends; the array of the current device is used, so `stream`
+ * must belong to it.  The call allocates nothing: no hipMalloc, no hipFree.
+ *   - A layer whose moe_workspace_size(layer, T) exceeds
+ *     MOE_STATIC_SCRATCH_BYTES is refused with MOE_ERR_SCRATCH_TOO_SMALL
+ *     before anything touches the GPU (the 16B-shaped layer fits up to about
+ *     1100 tokens, the decode batch of 128 with room to spare).
+ *   - Every call on a GPU shares that GPU's array and leaves its contents
+ *     behind; nothing in it needs to start at zero (each value the forward
+ *     reads from it is written earlier in the same call).  Calls that
+ *     overlap on one GPU (on different streams, or from several threads
+ *     without ordering) race on the array and give undefined results.
+ * Other arguments, checks and errors as moe_forward. */
+int moe_forward_noalloc(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
+                        const float* logit_bias, const void* w_gate, const void* w_up,
+                        const void* w_down, const void* ws_gate, const void* ws_up,
+                        const void* ws_down, const void* residual, void* y, int32_t* topk_idx,
+                        float* topk_w, int32_t* counts, int32_t* offsets, void* stream);
 
 #ifdef __cplusplus
 }

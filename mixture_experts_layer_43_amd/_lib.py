@@ -7,7 +7,9 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
-MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
+(MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP,
+ MOE_ERR_SCRATCH_TOO_SMALL) = range(6)
+MOE_STATIC_SCRATCH_BYTES = 64 * 1024 * 1024
 MOE_F32, MOE_BF16 = 0, 1
 MOE_GATE_SOFTMAX_TOPK, MOE_GATE_TOPK_SOFTMAX = 0, 1
 MOE_FFN_SILU_GATED, MOE_FFN_RELU = 0, 1
@@ -17,7 +19,7 @@ MOE_WEIGHTS_ROW_MAJOR, MOE_WEIGHTS_PACKED = 0, 1
 EXPORTS = (
     "moe_abi_version", "moe_status_str", "moe_last_hip_error", "moe_workspace_size",
     "moe_pack_weights", "moe_route", "moe_route_noisy", "moe_route_stats", "moe_permute", "moe_expert_ffn", "moe_shared_ffn", "moe_combine",
-    "moe_forward", "moe_forward_timed",
+    "moe_forward", "moe_forward_timed", "moe_forward_noalloc",
 )
 MOE_NUM_STAGES = 7
 STAGES = ("route", "dispatch", "routed_gate_up", "routed_down", "shared_gate_up", "shared_down",
@@ -61,6 +63,7 @@ _SIGS = {
     "moe_forward": ([LP, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
     "moe_forward_timed": ([LP, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P,
                            ctypes.POINTER(ctypes.c_void_p)], ctypes.c_int),
+    "moe_forward_noalloc": ([LP, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P], ctypes.c_int),
 }
 
 

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "kernels.h"
@@ -328,6 +329,8 @@ const char* moe_status_str(int status) {
     case MOE_ERR_UNSUPPORTED: return "unsupported shape, dtype or alignment";
     case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case MOE_ERR_HIP: return "HIP error";
+    case MOE_ERR_SCRATCH_TOO_SMALL:
+      return "the layer needs more scratch than the static buffer of moe_forward_noalloc holds";
     default: return "unknown status";
   }
 }
@@ -693,6 +696,63 @@ int moe_forward_timed(const moe_layer* layer, int64_t T, const void* x, const fl
   return forward_impl(layer, T, x, w_router, logit_bias, w_gate, w_up, w_down, ws_gate, ws_up,
                       ws_down, residual, y, topk_idx, topk_w, counts, offsets, ws, ws_bytes,
                       stream, reinterpret_cast<hipEvent_t const*>(events));
+}
+
+
+}  // extern "C"
+
+// ---- moe_forward_noalloc: scratch from a static device array ------------
+//
+// For callers that cannot allocate.  The forward's scratch (the same layout
+// moe_workspace_size describes) comes from `scratch`, a file-scope device
+// array of MOE_STATIC_SCRATCH_BYTES that each GPU holds from the first call
+// on it until the process ends.  In host code `scratch` names a host-side
+// stand-in, so the device address of each GPU's copy is looked up once
+// (hipGetSymbolAddress, with that device current) and only that address is
+// handed to the kernels.
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[MOE_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, looked up on the
+// first call on that device.
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  MOE_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    MOE_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+    if (ptr == nullptr) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward_noalloc(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
+                        const float* logit_bias, const void* w_gate, const void* w_up,
+                        const void* w_down, const void* ws_gate, const void* ws_up,
+                        const void* ws_down, const void* residual, void* y, int32_t* topk_idx,
+                        float* topk_w, int32_t* counts, int32_t* offsets, void* stream) {
+  MOE_TRY(check_layer(layer, T));
+  // Refused before the GPU is touched.
+  if (layout_of(layer, T).total > static_cast<size_t>(MOE_STATIC_SCRATCH_BYTES))
+    return MOE_ERR_SCRATCH_TOO_SMALL;
+  void* ws = nullptr;
+  MOE_TRY(scratch_of_current_device(&ws));
+  return forward_impl(layer, T, x, w_router, logit_bias, w_gate, w_up, w_down, ws_gate, ws_up,
+                      ws_down, residual, y, topk_idx, topk_w, counts, offsets, ws,
+                      static_cast<size_t>(MOE_STATIC_SCRATCH_BYTES), stream, nullptr);
 }
 
 }  // extern "C"

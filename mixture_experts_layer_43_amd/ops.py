@@ -231,15 +231,18 @@ def combine(layer: Layer, y_perm, slot_row, topk_w, y_shared=None, residual=None
 
 
 class Forward:
-    """The whole layer with preallocated outputs and workspace (repeat calls allocate nothing)."""
+    """The whole layer with preallocated outputs and workspace (repeat calls allocate nothing).
 
-    def __init__(self, layer: Layer, T: int, device):
+    noalloc=True calls moe_forward_noalloc instead: no workspace tensor, the
+    scratch comes from the library's static device array (include/moe.h)."""
+
+    def __init__(self, layer: Layer, T: int, device, noalloc: bool = False):
         device = torch.device(device)
         if device.type == "cuda" and device.index is None:
             device = torch.device("cuda", torch.cuda.current_device())
-        self.layer, self.T, self.device = layer, T, device
+        self.layer, self.T, self.device, self.noalloc = layer, T, device, noalloc
         self._c = layer.c()
-        self.ws = workspace(layer, T, device)
+        self.ws = None if noalloc else workspace(layer, T, device)
         self.y = torch.empty((T, layer.d_model), dtype=layer.torch_dtype, device=device)
         self.topk_idx = torch.empty((T, layer.top_k), dtype=torch.int32, device=device)
         self.topk_w = torch.empty((T, layer.top_k), dtype=torch.float32, device=device)
@@ -265,6 +268,12 @@ class Forward:
                  ws_down=None, residual=None, checked=False):
         if not checked:
             self.check(x, w_router, bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, residual)
+        if self.noalloc:
+            call("moe_forward_noalloc", ctypes.byref(self._c), self.T, _p(x), _p(w_router), _p(bias),
+                 _p(w_gate), _p(w_up), _p(w_down), _p(ws_gate), _p(ws_up), _p(ws_down),
+                 _p(residual), _p(self.y), _p(self.topk_idx), _p(self.topk_w), _p(self.counts),
+                 _p(self.offsets), _stream())
+            return self.y
         call("moe_forward", ctypes.byref(self._c), self.T, _p(x), _p(w_router), _p(bias),
              _p(w_gate), _p(w_up), _p(w_down), _p(ws_gate), _p(ws_up), _p(ws_down), _p(residual),
              _p(self.y), _p(self.topk_idx), _p(self.topk_w), _p(self.counts), _p(self.offsets),

@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     L = _lib.lib()
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib.EXPORTS)
@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     L = _lib.lib()
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
     assert _lib.status_str(MOE_OK) == "ok"
     assert "workspace" in _lib.status_str(MOE_ERR_WORKSPACE_TOO_SMALL)
     assert L.moe_last_hip_error() == 0
@@ -180,3 +180,23 @@ def test_python_binding_rejects_bad_shapes_without_gpu():
         ops.route(lay, torch.zeros(8, 32), torch.zeros(16, 64))      # wrong d
     with pytest.raises(ValueError):
         ops.route(lay, torch.zeros(8, 64), torch.zeros(16, 64))      # CPU tensors
+
+
+def test_noalloc_forward_refuses_a_batch_beyond_its_static_scratch():
+    """moe_forward_noalloc checks the layer's scratch need against
+    MOE_STATIC_SCRATCH_BYTES before touching the GPU."""
+    L = layer()
+    st, need = ws_size(L, 16384)
+    assert st == MOE_OK and need > _lib.MOE_STATIC_SCRATCH_BYTES
+    st = _lib.lib().moe_forward_noalloc(ctypes.byref(L), 16384, *([None] * 16))
+    # argument checks come first: null inputs are refused as for moe_forward
+    assert st in (MOE_ERR_INVALID_ARG, _lib.MOE_ERR_SCRATCH_TOO_SMALL)
+    fake = ctypes.c_void_p(1 << 20)            # aligned, never dereferenced
+    args = [fake] * 16
+    args[2] = None                             # logit_bias
+    args[9] = None                             # residual
+    st = _lib.lib().moe_forward_noalloc(ctypes.byref(L), 16384, *args)
+    assert st == _lib.MOE_ERR_SCRATCH_TOO_SMALL
+    assert "static" in _lib.status_str(st)
+    st = _lib.lib().moe_forward_noalloc(ctypes.byref(layer(top_k=0)), 8, *args)
+    assert st == MOE_ERR_INVALID_ARG
