@@ -33,10 +33,12 @@ the host cores, repeated until CPU_MIN_S of wall time have passed; `cores`
 is the BLAS thread count it ran with, `host_cpu_count` the host's cores.
 
 The `decode` object times the decode-shaped layer (the same 16B layer at
-T = DECODE_TOKENS) in the same run, DECODE_STEPS_MULT times as many steps
-(a step is about a tenth of a millisecond long): ms per step, the layer's
+T = 128) in the same run, DECODE_STEPS_MULT times as many steps (a step
+is about a quarter of a millisecond long): ms per step, the layer's
 fraction of the HBM roofline back to back and with a cold memory-side
-cache, and its gate/up kernel against HBM bandwidth.
+cache, and its gate/up kernel against HBM bandwidth.  `decode.graph`
+times the same forward captured once in a HIP graph and replayed (checked
+bit for bit against the eager forward first).
 """
 from __future__ import annotations
 
@@ -278,6 +280,64 @@ class Bench:
         del junk, sink
         return float(np.median(cold))
 
+    def graph(self):
+        """One moe_forward captured in a HIP graph (through torch.cuda.CUDAGraph on
+        the launch stream), checked against the eager result."""
+        import torch
+        y_eager = self.fwd.y.clone()
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                self.fwd(*self.call_args, checked=True)
+        torch.cuda.current_stream().wait_stream(side)
+        with torch.cuda.graph(g):
+            self.fwd(*self.call_args, checked=True)
+        g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(self.fwd.y, y_eager):
+            raise RuntimeError("graph replay of moe_forward differs from the eager forward")
+        return g
+
+    def graph_timed(self, g, steps, warmup):
+        """ms per replay of g, back to back, after warm-up replays."""
+        import torch
+        t_w = time.perf_counter()
+        n = 0
+        while n < warmup or time.perf_counter() - t_w < WARMUP_MIN_S:
+            g.replay()
+            n += 1
+            if n % 50 == 0:
+                torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(steps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    def graph_cold(self, g, n):
+        """Median ms of single replays, each after a clean 512 MB read."""
+        import numpy as np
+        import torch
+        junk = torch.ones(128 << 20, dtype=torch.int32, device=self.dev)
+        sink = torch.empty((), dtype=torch.int64, device=self.dev)
+        out = []
+        for _ in range(n):
+            torch.sum(junk, dim=0, dtype=torch.int64, out=sink)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b))
+        del junk, sink
+        return float(np.median(out))
+
     def layer_bytes(self):
         """Least bytes a forward moves: the weights of every expert it uses,
         the router weights, x and y."""
@@ -344,6 +404,12 @@ def decode_side(args, dev):
     cold_ms = b.cold_mall(max(5, min(args.steps, 20)))
     lb = b.layer_bytes()
     roof = b.gate_up_roofline(gu_ms)
+    # The same forward as a HIP graph: one submission per step, the way a
+    # decode loop that cannot afford per-kernel launches runs it.
+    g = b.graph()
+    g_ms = b.graph_timed(g, steps, args.warmup)
+    g_cold = b.graph_cold(g, max(5, min(args.steps, 20)))
+    del g
     b.close()
     out = {
         "workload": f"DeepSeekMoE {cfg.name} layer forward: T={cfg.tokens}, d={cfg.d_model}, "
@@ -358,6 +424,9 @@ def decode_side(args, dev):
         "cold_mall_layer_hbm_frac": lb / (cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "stage_ms": st,
         "roofline": roof,
+        "graph": {"ms_per_step": g_ms, "layer_hbm_frac": lb / (g_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                  "cold_mall_ms_per_step": g_cold,
+                  "cold_mall_layer_hbm_frac": lb / (g_cold * 1e-3) / 1e9 / PEAK_HBM_GBS},
     }
     del b
     torch.cuda.empty_cache()
