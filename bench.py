@@ -68,7 +68,11 @@ DECODE_STEPS_MULT = 10
 # was taken on; when the source differs the figure no longer describes the
 # kernel and roofline.traffic is null.
 GEMM_SOURCE = os.path.join(ROOT, "mixture_experts_layer_43_amd", "csrc", "gemm_bf16.hip")
-TRAFFIC_BYTES = {}
+TRAFFIC_BYTES = {
+    # profiles/moe_layer_16b_counters.md, profiles/moe_layer_16b-decode_counters.md
+    ("16b", "packed"): {"bytes": 3844063317, "gemm_sha": "30160e90877d8de0"},
+    ("16b-decode", "packed"): {"bytes": 769386965, "gemm_sha": "30160e90877d8de0"},
+}
 
 
 def gemm_source_sha() -> str:
@@ -99,6 +103,9 @@ def parse():
                     help="also run a plain 1 GiB device copy (for counter scaling)")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the decode-shaped layer's side measurement")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="also measure reference ceilings: a 1 GiB device copy and hipBLASLt (torch.matmul) "
+                         "on the dense equivalents of the expert GEMMs")
     ap.add_argument("--no-extras", action="store_true",
                     help="time the forward only (no breakdown, capacity, statistics or other layout)")
     return ap.parse_args()
@@ -390,6 +397,39 @@ def per_call_ms(fn, n=20):
     return a.elapsed_time(b) / n
 
 
+def ceilings(dev):
+    """Reference ceilings on this GPU, measured in the same process: the HBM
+    rate of a plain 1 GiB device copy (bytes read + written), and hipBLASLt
+    bf16 GEMMs (through torch.matmul, normal random data) of the dense shapes
+    that the 16b layer's expert GEMMs would be without routing: M rows of
+    activations (the routed rows, and routed + shared) against one weight
+    matrix of the gate/up (N = 2 I) or down (N = d) shape."""
+    import torch
+    out = {}
+    a = torch.empty(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
+    b = torch.empty_like(a)
+    out["copy_1gib_gbs"] = 2.0 * a.numel() * 2 / (per_call_ms(lambda: b.copy_(a), n=10) * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    g = torch.Generator(device=dev).manual_seed(43)
+    gemms = {}
+    for name, (M, N, K) in {"gate_up_routed": (98304, 2816, 2048), "gate_up_all": (131072, 2816, 2048),
+                            "down_routed": (98304, 2048, 1408), "down_all": (131072, 2048, 1408)}.items():
+        x = torch.randn(M, K, device=dev, dtype=torch.bfloat16, generator=g)
+        w = torch.randn(K, N, device=dev, dtype=torch.bfloat16, generator=g) * (K ** -0.5)
+        y = torch.empty(M, N, device=dev, dtype=torch.bfloat16)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < WARMUP_MIN_S:
+            torch.matmul(x, w, out=y)
+            torch.cuda.synchronize()
+        ms = per_call_ms(lambda: torch.matmul(x, w, out=y), n=10)
+        gemms[name] = {"M": M, "N": N, "K": K, "ms": ms, "tflops": 2.0 * M * N * K / (ms * 1e-3) / 1e12}
+        del x, w, y
+        torch.cuda.empty_cache()
+    out["hipblaslt_bf16"] = gemms
+    return out
+
+
 def decode_side(args, dev):
     """The decode-shaped layer, measured in the same run (not the bench line's value)."""
     import torch
@@ -577,6 +617,10 @@ def main():
     inputs = b.inputs
     del b
     torch.cuda.empty_cache()
+
+    if args.ceilings:
+        print("[bench] reference ceilings", file=sys.stderr, flush=True)
+        out["ceilings"] = ceilings(dev)
 
     if not args.no_decode and cfg.name != DECODE_WORKLOAD:
         print(f"[bench] decode-shaped layer {DECODE_WORKLOAD}", file=sys.stderr, flush=True)
