@@ -257,6 +257,32 @@ def test_small_batches(T):
     check_y(host(f.y), ref["y"], cfg.dtype)
 
 
+@pytest.mark.parametrize("name,T", [("16b-decode", 1), ("16b-decode", 17), ("16b-decode", 128),
+                                    ("16b-decode", 256), ("mid-ragged", 200), ("mid-gshard", 100),
+                                    ("mid-wide-k", 200)])
+def test_forward_small_batch_routing_equals_staged_calls(name, T):
+    """Small batches route inside moe_forward with K split over workgroups and
+    a separate selection; its choices, counts and offsets are the same as
+    moe_route followed by moe_permute (moe_route sums K in one workgroup, so
+    the gate values may differ in the last bits and are held to the gate
+    tolerance), and everything matches the oracle."""
+    cfg = cfg_of(name).with_(tokens=T, seed=500 + T)
+    announce(f"small-batch routing {name} T={T}")
+    inp = prepare(cfg)
+    d = upload(inp)
+    lay = ops.Layer.of(cfg)
+    idx, w = ops.route(lay, d["x"], d["w_router"], d["bias"])
+    pm = ops.permute(lay, idx, None)
+    f = run_forward(cfg, d)
+    assert torch.equal(f.topk_idx, idx)
+    check_gates(host(f.topk_w), host(w))
+    assert torch.equal(f.counts, pm["counts"])
+    assert torch.equal(f.offsets, pm["offsets"])
+    ref = oracle.forward(cfg, inp)
+    check_routing(f, ref)
+    check_y(host(f.y), ref["y"], cfg.dtype)
+
+
 @pytest.mark.parametrize("k", [1, 2])
 def test_all_tokens_to_few_experts(k):
     """A large router bias sends every token to the same k experts; the other
