@@ -283,6 +283,27 @@ def test_forward_small_batch_routing_equals_staged_calls(name, T):
     check_y(host(f.y), ref["y"], cfg.dtype)
 
 
+@pytest.mark.parametrize("name,T", [("16b", 16384), ("2b", 8192), ("gshard-zipf", 4096),
+                                    ("mid-many-experts", 5000)])
+def test_forward_large_batch_routing_equals_route(name, T):
+    """Large batches route inside moe_forward with the unsplit matrix-core
+    router, as moe_route does: the same operands in the same order, so the
+    choices and gates are the same bits, and they match the oracle."""
+    cfg = cfg_of(name).with_(tokens=T)
+    announce(f"large-batch routing {name} T={T}")
+    inp = prepare(cfg)
+    d = upload(inp)
+    lay = ops.Layer.of(cfg)
+    idx, w = ops.route(lay, d["x"], d["w_router"], d["bias"])
+    f = run_forward(cfg, d)
+    assert torch.equal(f.topk_idx, idx)
+    assert torch.equal(f.topk_w, w)
+    ref = oracle.forward(cfg, inp, tokens=np.zeros(0, dtype=np.int64))
+    check_routing(f, ref)
+    del d, f
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("k", [1, 2])
 def test_all_tokens_to_few_experts(k):
     """A large router bias sends every token to the same k experts; the other
