@@ -38,7 +38,7 @@
  *     MOE_ERR_HIP and moe_last_hip_error() gives the hipError_t.  Faults
  *     inside kernels surface at the caller's next synchronisation.
  *   - Requirements (else MOE_ERR_UNSUPPORTED): N_r <= 256, 1 <= K' <= 16,
- *     K' <= N_r; for MOE_BF16, d % 64 == 0, I % 64 == 0, I_s % 64 == 0;
+ *     K' <= N_r; for MOE_BF16, d % 8 == 0, I % 16 == 0, I_s % 16 == 0;
  *     for MOE_F32, d % 4 == 0, I % 4 == 0, I_s % 4 == 0; T < 2^31 / 16;
  *     every activation and weight matrix (x, x_perm, y_perm, the T*K' x I
  *     and T x K_s*I_s intermediates, one expert's weights) below 4 GB;

@@ -115,9 +115,13 @@ int check_layer(const moe_layer* L, int64_t T) {
   if (R * std::max(L->d_model, L->d_ff) * e >= lim || T * wsh * e >= lim ||
       wsh * L->d_model * e >= lim || static_cast<int64_t>(L->d_ff) * L->d_model * e >= lim)
     return MOE_ERR_UNSUPPORTED;
-  const int q = (L->dtype == MOE_BF16) ? 64 : 4;
-  if (L->d_model % q != 0 || L->d_ff % q != 0) return MOE_ERR_UNSUPPORTED;
-  if (L->n_shared > 0 && L->d_ff_shared % q != 0) return MOE_ERR_UNSUPPORTED;
+  // bf16: rows move in 16-byte chunks of 8 values (d % 8) and expert widths
+  // are multiples of 16 (I, I_s); neither has to fill whole 64-wide K steps
+  // of the GEMMs.  f32: 16-byte chunks of 4 values.
+  const int qd = (L->dtype == MOE_BF16) ? 8 : 4;
+  const int qi = (L->dtype == MOE_BF16) ? 16 : 4;
+  if (L->d_model % qd != 0 || L->d_ff % qi != 0) return MOE_ERR_UNSUPPORTED;
+  if (L->n_shared > 0 && L->d_ff_shared % qi != 0) return MOE_ERR_UNSUPPORTED;
   if (L->weight_layout == MOE_WEIGHTS_PACKED) {
     // Packed tiles are kPackRows rows of every expert matrix (I rows of W1/W3,
     // d rows of W2) and bf16 only.

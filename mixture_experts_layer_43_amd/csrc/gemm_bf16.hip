@@ -15,8 +15,11 @@
 // is a plain A . B^T.  Operands go global -> LDS directly
 // (global_load_lds_dwordx4, no staging registers; two stages; 16-byte chunks
 // in XOR-swizzled rows so the 16-byte fragment reads of a quarter-wave hit
-// distinct banks) -> v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  Workgroup ids are remapped so that consecutive tiles run on
-// the same XCD and share its L2.
+// distinct banks) -> v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
+// Workgroup ids are remapped so that consecutive tiles run on the same XCD
+// and share its L2.  A K that is a multiple of 8 but not of BK takes a
+// separate instantiation (RAGGED) whose last step per weight matrix is
+// partial; the aligned instantiation does not carry its checks.
 #include "common.h"
 #include <hip/hip_ext.h>
 
@@ -152,6 +155,41 @@ __device__ __forceinline__ void copy_step(__amdgpu_buffer_rsrc_t ra, __amdgpu_bu
                                              b_off[i], sb, 0, 0);
 }
 
+// Ragged K: the K of one sub-matrix (k_sub) is a multiple of 8 but not of
+// BK (row-major B only).  A sub-matrix then takes sps = ceil(k_sub / BK)
+// steps, and its last one holds kvalid = k_sub - kin < BK values.  Step kt
+// covers k in [sub*k_sub + kin, +BK) of A and column kin of sub-matrix sub
+// of B.  A lane whose 16-byte chunk lies past kvalid copies its row's first
+// chunk of the step instead, so every address stays inside the row; the B
+// fragments of those chunks are zeroed before the MFMAs (mask_b).
+template <int BM, int BK, int A_LD, int B_LD>
+__device__ __forceinline__ void copy_step_ragged(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                                 const uint32_t (&a_off)[A_LD],
+                                                 const uint32_t (&b_off)[B_LD], int kt, int sps,
+                                                 int k_sub, int64_t b_sub_stride, int wv, int lane,
+                                                 bf16_t* __restrict__ s) {
+  constexpr int R = kWave / (BK / 8);
+  const int sub = kt / sps;
+  const int kin = (kt - sub * sps) * BK;
+  const int kvalid = k_sub - kin;
+  const uint32_t sa = static_cast<uint32_t>(sub * k_sub + kin) * 2u;
+  const uint32_t sb = static_cast<uint32_t>((static_cast<int64_t>(sub) * b_sub_stride + kin) * 2);
+  const int lr = lane / (BK / 8), lp = lane % (BK / 8);
+#pragma unroll
+  for (int i = 0; i < A_LD; ++i) {
+    const int c = lp ^ swz<BK>((wv * A_LD + i) * R + lr);
+    const uint32_t o = c * 8 < kvalid ? a_off[i] : a_off[i] - static_cast<uint32_t>(c * 16);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds_ptr(s + (wv * A_LD + i) * R * BK), 16, o, sa, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < B_LD; ++i) {
+    const int c = lp ^ swz<BK>((wv * B_LD + i) * R + lr);
+    const uint32_t o = c * 8 < kvalid ? b_off[i] : b_off[i] - static_cast<uint32_t>(c * 16);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, lds_ptr(s + BM * BK + (wv * B_LD + i) * R * BK), 16, o,
+                                             sb, 0, 0);
+  }
+}
+
 // Fragments of one 16-wide K slice: lane l holds 8 consecutive k of tile row
 // a_row/b_row (= l%32 within its 32-row block), K half l/32.  Only the
 // first MBA of the MB row blocks are read and multiplied: row blocks past
@@ -184,6 +222,16 @@ __device__ __forceinline__ void mma_slice(f32x16 (&acc)[MB][NB], const Frags<MB,
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[buf][i], f.b[buf][j], acc[i][j], 0, 0, 0);
 }
 
+// Ragged K: B fragments of logical chunk c (k = 8c .. 8c+7 of the step) at
+// or past kvalid become zero, so the chunk adds nothing to the products.
+template <int MB, int NB>
+__device__ __forceinline__ void mask_b(Frags<MB, NB>& f, int buf, int c, int kvalid) {
+  if (c * 8 >= kvalid) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) f.b[buf][j] = bf16x8{};
+  }
+}
+
 // Scheduling pattern for one slice's MBA*NB MFMAs with the MBA+NB fragment
 // reads of the next slice spread between them.
 template <int MBA, int NB>
@@ -204,12 +252,13 @@ __device__ __forceinline__ void interleave() {
 // step is read, so the matrix cores have work across the barrier.  The last
 // slice of this step is only read here; its MFMAs run in the next step (or
 // after the loop).
-template <int BM, int BK, int MB, int NB, int MBA>
+template <int BM, int BK, int MB, int NB, int MBA, bool RAGGED>
 __device__ __forceinline__ void step_body(f32x16 (&acc)[MB][NB], Frags<MB, NB>& f,
                                           const bf16_t* __restrict__ cur, bool has_prev, int khalf,
-                                          const int (&a_row)[MB], const int (&b_row)[NB]) {
+                                          const int (&a_row)[MB], const int (&b_row)[NB], int kvalid) {
   constexpr int NS = BK / 16;
   read_slice<BM, BK, MB, NB, MBA>(f, cur, 0, 0, khalf, a_row, b_row);
+  if constexpr (RAGGED) mask_b(f, 0, khalf, kvalid);
   if (has_prev) {
     mma_slice<MB, NB, MBA>(acc, f, 1);
     interleave<MBA, NB>();
@@ -219,6 +268,7 @@ __device__ __forceinline__ void step_body(f32x16 (&acc)[MB][NB], Frags<MB, NB>& 
 #pragma unroll
   for (int kk = 0; kk + 1 < NS; ++kk) {
     read_slice<BM, BK, MB, NB, MBA>(f, cur, kk + 1, (kk + 1) & 1, khalf, a_row, b_row);
+    if constexpr (RAGGED) mask_b(f, (kk + 1) & 1, (kk + 1) * 2 + khalf, kvalid);
     mma_slice<MB, NB, MBA>(acc, f, kk & 1);
     interleave<MBA, NB>();
   }
@@ -231,32 +281,41 @@ __device__ __forceinline__ void step_body(f32x16 (&acc)[MB][NB], Frags<MB, NB>& 
 // any more), issues the copy of step kt+STAGES-1 into that stage and
 // computes.  A wavefront whose rows are all past the tile's last row
 // (MBA == 0) only copies and waits.
-template <int BM, int BK, int STAGES, int MB, int NB, int MBA, int A_LD, int B_LD>
+template <int BM, int BK, int STAGES, int MB, int NB, int MBA, int A_LD, int B_LD, bool RAGGED>
 __device__ __forceinline__ void k_loop(f32x16 (&acc)[MB][NB], __amdgpu_buffer_rsrc_t ra,
                                        __amdgpu_buffer_rsrc_t rb, const uint32_t (&a_off)[A_LD],
                                        const uint32_t (&b_off)[B_LD], int nk, int k_sub,
                                        int64_t kstride_b, bool packed, int wv, int khalf,
                                        const int (&a_row)[MB],
-                                       const int (&b_row)[NB], bf16_t* smem, int se) {
+                                       const int (&b_row)[NB], bf16_t* smem, int se, int sps,
+                                       int lane) {
   constexpr int L = A_LD + B_LD;
   Frags<MB, NB> fr;
   for (int kt = 0; kt < nk; ++kt) {
     wait_steps<L, STAGES>(min(STAGES - 2, nk - 1 - kt));
     lds_barrier();
     const int kn = kt + STAGES - 1;
-    if (kn < nk)
-      copy_step<BM, BK, A_LD, B_LD>(ra, rb, a_off, b_off, kn * BK, k_sub, kstride_b, packed, wv,
-                                    smem + (kn % STAGES) * se);
+    if (kn < nk) {
+      if constexpr (RAGGED)
+        copy_step_ragged<BM, BK, A_LD, B_LD>(ra, rb, a_off, b_off, kn, sps, k_sub, kstride_b, wv, lane,
+                                             smem + (kn % STAGES) * se);
+      else
+        copy_step<BM, BK, A_LD, B_LD>(ra, rb, a_off, b_off, kn * BK, k_sub, kstride_b, packed, wv,
+                                      smem + (kn % STAGES) * se);
+    }
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (MBA > 0)
-      step_body<BM, BK, MB, NB, MBA>(acc, fr, smem + (kt % STAGES) * se, kt > 0, khalf, a_row, b_row);
+    if constexpr (MBA > 0) {
+      const int kvalid = RAGGED ? k_sub - (kt % sps) * BK : BK;
+      step_body<BM, BK, MB, NB, MBA, RAGGED>(acc, fr, smem + (kt % STAGES) * se, kt > 0, khalf, a_row,
+                                             b_row, kvalid);
+    }
   }
   if constexpr (MBA > 0) mma_slice<MB, NB, MBA>(acc, fr, 1);
 }
 
 // GROUPED: rows come in per-expert groups described by offsets (routed
 // experts); otherwise one dense group (shared experts).
-template <int BM, int BN, int WM, int WN, int BK, int STAGES, int MODE, bool GROUPED>
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int MODE, bool GROUPED, bool RAGGED>
 __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr int TM = BM / WM;               // rows per wavefront
@@ -446,18 +505,28 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
   }
 
   // ---- K loop -------------------------------------------------------------
-  const int nk = p.K / BK;
+  // K steps: BK-wide runs of K; with ragged K, ceil(k_sub / BK) per
+  // sub-matrix (p.K is a whole number of sub-matrices).
+  const int sps = RAGGED ? (p.k_sub + BK - 1) / BK : p.k_sub / BK;
+  const int nk = RAGGED ? (p.K / p.k_sub) * sps : p.K / BK;
   const int64_t kstride_b = p.b_sub_stride;
 #pragma unroll
-  for (int j = 0; j < STAGES - 1; ++j)
-    if (j < nk) copy_step<BM, BK, A_LD, B_LD>(ra, rb, a_off, b_off, j * BK, p.k_sub, kstride_b, p.packed, wv,
-                                               smem + j * SE);
+  for (int j = 0; j < STAGES - 1; ++j) {
+    if (j < nk) {
+      if constexpr (RAGGED)
+        copy_step_ragged<BM, BK, A_LD, B_LD>(ra, rb, a_off, b_off, j, sps, p.k_sub, kstride_b, wv, lane,
+                                             smem + j * SE);
+      else
+        copy_step<BM, BK, A_LD, B_LD>(ra, rb, a_off, b_off, j * BK, p.k_sub, kstride_b, p.packed, wv,
+                                      smem + j * SE);
+    }
+  }
   // 32-row blocks of this wavefront that hold rows of the tile.
   const int mba = __builtin_amdgcn_readfirstlane(max(0, min(MB, (rows - wm * TM + 31) / 32)));
 #define MOE_K_LOOP(n)                                                                            \
-  k_loop<BM, BK, STAGES, MB, NB, n, A_LD, B_LD>(acc, ra, rb, a_off, b_off, nk, p.k_sub, kstride_b, \
-                                                p.packed, \
-                                                wv, khalf, a_row, b_row, smem, SE)
+  k_loop<BM, BK, STAGES, MB, NB, n, A_LD, B_LD, RAGGED>(acc, ra, rb, a_off, b_off, nk, p.k_sub,   \
+                                                        kstride_b, p.packed, wv, khalf, a_row,     \
+                                                        b_row, smem, SE, sps, lane)
   if (mba == MB) {
     MOE_K_LOOP(MB);
   } else if (mba == 0) {
@@ -603,12 +672,22 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s, StageEvents ev) {
   const int64_t grid = max_mtiles * n_ntiles;
   if (grid == 0) return record_stage(ev, s);
   const dim3 block(WM * WN * kWave);
-  if (a.offsets != nullptr)
-    hipExtLaunchKernelGGL((grouped_gemm_bf16<BM, BN, WM, WN, BK, STAGES, MODE, true>), dim3(grid), block, 0,
-                          s, ev.start, ev.stop, 0, a);
-  else
-    hipExtLaunchKernelGGL((grouped_gemm_bf16<BM, BN, WM, WN, BK, STAGES, MODE, false>), dim3(grid), block, 0,
-                          s, ev.start, ev.stop, 0, a);
+  // K must be whole sub-matrices; ragged sub-matrices (k_sub not a multiple
+  // of BK, still of 8) take the ragged instantiation, row-major B only.
+  if (a.k_sub <= 0 || a.k_sub % 8 != 0 || a.K % a.k_sub != 0) return hipErrorInvalidValue;
+  const bool ragged = a.k_sub % BK != 0;
+  if (ragged && a.packed) return hipErrorInvalidValue;
+#define MOE_GEMM_LAUNCH(G, R)                                                                        \
+  hipExtLaunchKernelGGL((grouped_gemm_bf16<BM, BN, WM, WN, BK, STAGES, MODE, G, R>), dim3(grid), block, 0, \
+                        s, ev.start, ev.stop, 0, a)
+  if (a.offsets != nullptr) {
+    if (ragged) MOE_GEMM_LAUNCH(true, true);
+    else MOE_GEMM_LAUNCH(true, false);
+  } else {
+    if (ragged) MOE_GEMM_LAUNCH(false, true);
+    else MOE_GEMM_LAUNCH(false, false);
+  }
+#undef MOE_GEMM_LAUNCH
   return hipGetLastError();
 }
 

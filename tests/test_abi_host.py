@@ -70,9 +70,12 @@ def test_workspace_size_scales_with_tokens():
     (dict(n_routed=0), 8, MOE_ERR_INVALID_ARG),
     (dict(), -1, MOE_ERR_INVALID_ARG),
     (dict(n_routed=300), 8, MOE_ERR_UNSUPPORTED),
-    (dict(d_model=2000), 8, MOE_ERR_UNSUPPORTED),
-    (dict(d_ff=1400), 8, MOE_ERR_UNSUPPORTED),
+    (dict(d_model=2004), 8, MOE_ERR_UNSUPPORTED),                 # bf16: d % 8
+    (dict(d_model=2000), 8, MOE_OK),                              # d need not fill 64-wide K steps
+    (dict(d_ff=1400), 8, MOE_ERR_UNSUPPORTED),                    # bf16: I % 16
+    (dict(d_ff=1392, d_ff_shared=1392), 8, MOE_OK),
     (dict(d_ff_shared=100), 8, MOE_ERR_UNSUPPORTED),
+    (dict(d_ff_shared=112), 8, MOE_OK),
     (dict(dtype=MOE_F32, d_model=62), 8, MOE_ERR_UNSUPPORTED),
     (dict(dtype=MOE_F32, d_model=60, d_ff=36, d_ff_shared=36), 8, MOE_OK),
     (dict(n_shared=0, d_ff_shared=0), 8, MOE_OK),
@@ -81,6 +84,7 @@ def test_workspace_size_scales_with_tokens():
     (dict(capacity=5, group_size=64), 8, MOE_OK),
     (dict(weight_layout=1), 8, MOE_OK),                            # d, I, I_s multiples of 128
     (dict(weight_layout=1, d_ff=1344, d_ff_shared=1344), 8, MOE_ERR_UNSUPPORTED),
+    (dict(weight_layout=1, d_model=2000), 8, MOE_ERR_UNSUPPORTED),
     (dict(weight_layout=1, dtype=MOE_F32), 8, MOE_ERR_UNSUPPORTED),
     (dict(weight_layout=5), 8, MOE_ERR_INVALID_ARG),
 ])

@@ -41,7 +41,25 @@ MID = {
     # More tokens than the single-workgroup dispatch takes (1024).
     "mid-many-tokens": LayerConfig(name="mid-many-tokens", tokens=2500, d_model=64, n_routed=24,
                                    n_shared=1, top_k=5, d_ff=64, d_ff_shared=64, seed=108),
+    # d and I that do not fill whole 64-wide K steps of the GEMMs (d % 8,
+    # I % 16): the last K step of every row is partial.  Unfolded shared
+    # experts (I_s != I) whose down projection runs K over K_s matrices of
+    # width 112 (a step straddles no matrix boundary: each matrix ends in
+    # its own partial step).  Mean rows per expert reach the 128-row tiles.
+    "mid-ragged-k": LayerConfig(name="mid-ragged-k", tokens=700, d_model=200, n_routed=16, n_shared=2,
+                                top_k=4, d_ff=176, d_ff_shared=112, seed=110),
+    # Folded shared expert; 256-row tiles; last K steps of 8 (d) and 16 (I).
+    "mid-ragged-k-fold": LayerConfig(name="mid-ragged-k-fold", tokens=2400, d_model=328, n_routed=8,
+                                     n_shared=1, top_k=2, d_ff=144, d_ff_shared=144, seed=111),
+    # d below one K step (40), the narrowest expert (16); few rows per
+    # expert, so the 32-row tiles.
+    "mid-ragged-k-small": LayerConfig(name="mid-ragged-k-small", tokens=64, d_model=40, n_routed=32,
+                                      n_shared=1, top_k=4, d_ff=16, d_ff_shared=48, seed=112),
+    # Decode-sized batch of a 16B-like layer with d = 2040 and I = 1392.
+    "decode-ragged-k": LayerConfig(name="decode-ragged-k", tokens=128, d_model=2040, n_routed=64,
+                                   n_shared=2, top_k=6, d_ff=1392, d_ff_shared=1392, seed=113),
 }
+RAGGED_K = ["mid-ragged-k", "mid-ragged-k-fold", "mid-ragged-k-small", "decode-ragged-k"]
 FULL_ORACLE = ["tiny-f32", "16b-decode", *MID]
 # The full-size layers: the oracle evaluates every token of these as well
 # (a few seconds to some tens of seconds of host BLAS each).
@@ -98,7 +116,8 @@ def check_routing(f, ref):
 
 
 @pytest.mark.parametrize("name", ["tiny-f32", "mid-ragged", "mid-gshard", "mid-wide-k",
-                                  "mid-many-experts", "mid-max-experts", "mid-smallm", "2b"])
+                                  "mid-many-experts", "mid-max-experts", "mid-smallm", "2b",
+                                  "mid-ragged-k", "decode-ragged-k"])
 def test_route_alone(name):
     cfg, inp, ref = case(name)
     announce(f"route {name}")
@@ -143,7 +162,8 @@ def ref_rows(cfg, inp, ref):
     return out
 
 
-@pytest.mark.parametrize("name", ["tiny-f32", "mid-ragged", "mid-smallm", "mid-medm", "mid-f32"])
+@pytest.mark.parametrize("name", ["tiny-f32", "mid-ragged", "mid-smallm", "mid-medm", "mid-f32",
+                                  *RAGGED_K])
 def test_expert_ffn_alone(name):
     cfg, inp, ref = case(name)
     announce(f"expert_ffn {name}")
@@ -157,7 +177,8 @@ def test_expert_ffn_alone(name):
     check_y(host(y_perm), ref_rows(cfg, inp, ref), cfg.dtype, "y_perm")
 
 
-@pytest.mark.parametrize("name", ["tiny-f32", "mid-ragged", "mid-smallm", "mid-f32", "mid-medm"])
+@pytest.mark.parametrize("name", ["tiny-f32", "mid-ragged", "mid-smallm", "mid-f32", "mid-medm",
+                                  *RAGGED_K])
 def test_shared_ffn_alone(name):
     cfg, inp, ref = case(name)
     announce(f"shared_ffn {name}")
