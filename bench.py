@@ -268,17 +268,20 @@ class Bench:
         return dict(zip(_lib.STAGES, st.mean(0).round(5).tolist()))
 
     def cold_mall(self, n):
-        """Median ms of single forwards, each after a clean 512 MB read that
-        evicts the 256 MB memory-side cache."""
+        """Median ms of single forwards, each right after a clean 512 MB read
+        that evicts the 256 MB memory-side cache.  The read, the start event
+        and the forward are enqueued together, so the forward's kernels are
+        queued before the GPU reaches the start event and the time holds no
+        host launch latency."""
         import numpy as np
         import torch
         junk = torch.ones(128 << 20, dtype=torch.int32, device=self.dev)
         sink = torch.empty((), dtype=torch.int64, device=self.dev)
         cold = []
         for _ in range(n):
-            torch.sum(junk, dim=0, dtype=torch.int64, out=sink)
             torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.sum(junk, dim=0, dtype=torch.int64, out=sink)
             a.record()
             self.fwd(*self.call_args, checked=True)
             b.record()
@@ -327,16 +330,17 @@ class Bench:
         return a.elapsed_time(b) / steps
 
     def graph_cold(self, g, n):
-        """Median ms of single replays, each after a clean 512 MB read."""
+        """Median ms of single replays, each right after a clean 512 MB read
+        (enqueued together, as in cold_mall)."""
         import numpy as np
         import torch
         junk = torch.ones(128 << 20, dtype=torch.int32, device=self.dev)
         sink = torch.empty((), dtype=torch.int64, device=self.dev)
         out = []
         for _ in range(n):
-            torch.sum(junk, dim=0, dtype=torch.int64, out=sink)
             torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.sum(junk, dim=0, dtype=torch.int64, out=sink)
             a.record()
             g.replay()
             b.record()
