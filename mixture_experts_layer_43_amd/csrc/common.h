@@ -45,24 +45,64 @@ template <> struct Elt<bf16_t> {
   static __device__ __forceinline__ bf16_t from_f32(float v) { return f32_to_bf16(v); }
 };
 
-// Reductions over aligned groups of W lanes (W a power of two <= 64).
+// Value of the lane O places along inside this lane's row of 16 (DPP
+// row_ror; no trip through LDS).
+template <int O>
+__device__ __forceinline__ int row_ror(int v) {
+  static_assert(O >= 1 && O <= 15, "row rotation");
+  return __builtin_amdgcn_update_dpp(0, v, 0x120 + O, 0xF, 0xF, false);
+}
+template <int O>
+__device__ __forceinline__ float row_ror(float v) {
+  return __int_as_float(row_ror<O>(__float_as_int(v)));
+}
+
+// Reductions over aligned groups of W lanes (W a power of two <= 64): a
+// butterfly over the offsets W/2, ..., 2, 1, each lane combining its value
+// with that of lane i ^ o.  Groups of 16 (a DPP row) take the partner by a
+// row rotation by o instead: before the step with offset o every lane
+// already holds the same value as the lanes i ^ 2o, i ^ 4o, ..., so lane
+// i + o (mod 16), whichever way the row turns, holds the value of lane
+// i ^ o.  The combined operands, and so the results, are those of the xor
+// shuffles bit for bit.
 template <int W>
 __device__ __forceinline__ float group_max(float v) {
+  if constexpr (W == 16) {
+    v = fmaxf(v, row_ror<8>(v));
+    v = fmaxf(v, row_ror<4>(v));
+    v = fmaxf(v, row_ror<2>(v));
+    return fmaxf(v, row_ror<1>(v));
+  } else {
 #pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+    for (int o = W / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+  }
 }
 template <int W>
 __device__ __forceinline__ float group_sum(float v) {
+  if constexpr (W == 16) {
+    v += row_ror<8>(v);
+    v += row_ror<4>(v);
+    v += row_ror<2>(v);
+    return v + row_ror<1>(v);
+  } else {
 #pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+    for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+  }
 }
 template <int W>
 __device__ __forceinline__ int group_min_int(int v) {
+  if constexpr (W == 16) {
+    v = min(v, row_ror<8>(v));
+    v = min(v, row_ror<4>(v));
+    v = min(v, row_ror<2>(v));
+    return min(v, row_ror<1>(v));
+  } else {
 #pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
-  return v;
+    for (int o = W / 2; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
+    return v;
+  }
 }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
