@@ -59,7 +59,8 @@ def test_permute_with_capacity_is_bit_exact(name, factor, S, copy):
 
 FORWARD = [("mid-ragged", 1.0, 0), ("mid-ragged", 0.7, 128), ("mid-smallm", 1.0, 50),
            ("mid-gshard", 1.0, 0), ("mid-gshard", 1.25, 200), ("mid-f32", 1.0, 0),
-           ("mid-medm", 1.0, 64), ("16b-decode", 1.0, 0), ("mid-max-experts", 1.5, 100)]
+           ("mid-medm", 1.0, 64), ("16b-decode", 1.0, 0), ("mid-max-experts", 1.5, 100),
+           ("mid-ragged-k-fold", 0.8, 300)]
 
 
 @pytest.mark.parametrize("name,factor,S", FORWARD, ids=[f"{n}-f{f}-S{S}" for n, f, S in FORWARD])

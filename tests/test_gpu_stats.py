@@ -65,7 +65,8 @@ def run_case(cfg, inp, D, want_lse=True):
 
 CASES = [("tiny-f32", 4), ("mid-ragged", 4), ("mid-ragged", 1), ("mid-ragged", 16),
          ("mid-gshard", 2), ("mid-f32", 3), ("mid-wide-k", 10), ("mid-many-experts", 8),
-         ("mid-many-tokens", 6), ("mid-max-experts", 16), ("16b-decode", 8), ("2b", 9), ("16b", 8), ("gshard-zipf", 8)]
+         ("mid-many-tokens", 6), ("mid-max-experts", 16), ("16b-decode", 8), ("2b", 9), ("16b", 8), ("gshard-zipf", 8),
+         ("mid-ragged-k", 4), ("decode-ragged-k", 8)]
 
 
 @pytest.mark.parametrize("name,D", CASES, ids=[f"{n}-D{D}" for n, D in CASES])

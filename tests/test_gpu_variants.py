@@ -23,7 +23,8 @@ from test_gpu_stats import check_stats
 pytestmark = pytest.mark.gpu
 
 RELU = [("mid-ragged", {}), ("mid-gshard", {}), ("mid-f32", {}), ("16b-decode", {}),
-        ("mid-smallm", dict(capacity=6, group_size=100)), ("tiny-f32", {})]
+        ("mid-smallm", dict(capacity=6, group_size=100)), ("tiny-f32", {}), ("mid-ragged-k", {}),
+        ("decode-ragged-k", {})]
 
 
 @pytest.mark.parametrize("name,kw", RELU, ids=[f"{n}{'-cap' if kw else ''}" for n, kw in RELU])
