@@ -355,6 +355,35 @@ def test_top_k_equals_n_routed(gate):
     check_y(host(f.y), ref["y"], cfg.dtype)
 
 
+# The smallest layers the boundary accepts: one routed expert (every token
+# to it, gate 1), d = 8 (one 16-byte chunk per row) and I = 16; two experts
+# with top-1 and an unfolded shared expert; and one bf16 token.
+TINY_EDGE = {
+    "one-expert": LayerConfig(name="one-expert", tokens=5, d_model=8, n_routed=1, n_shared=0, top_k=1,
+                              d_ff=16, d_ff_shared=16, seed=601),
+    "two-experts-shared": LayerConfig(name="two-experts-shared", tokens=37, d_model=16, n_routed=2,
+                                      n_shared=1, top_k=1, d_ff=16, d_ff_shared=32, seed=602),
+    "one-token": LayerConfig(name="one-token", tokens=1, d_model=72, n_routed=5, n_shared=2, top_k=3,
+                             d_ff=48, d_ff_shared=48, gate="topk_softmax", seed=603),
+    "one-expert-f32": LayerConfig(name="one-expert-f32", tokens=9, d_model=4, n_routed=1, n_shared=1,
+                                  top_k=1, d_ff=4, d_ff_shared=8, dtype="f32", seed=604),
+}
+
+
+@pytest.mark.parametrize("name", sorted(TINY_EDGE))
+def test_smallest_layers(name):
+    cfg = TINY_EDGE[name]
+    announce(f"smallest layer {name}")
+    inp = prepare(cfg)
+    ref = oracle.forward(cfg, inp)
+    f = run_forward(cfg, upload(inp))
+    check_routing(f, ref)
+    check_y(host(f.y), ref["y"], cfg.dtype)
+    if cfg.n_routed == 1:
+        assert np.all(host(f.topk_idx) == 0)
+        np.testing.assert_array_equal(host(f.topk_w), 1.0)
+
+
 def test_repeat_calls_are_deterministic():
     cfg, inp, _ = case("mid-ragged")
     announce("determinism")
