@@ -732,7 +732,20 @@ hipError_t record_stage(StageEvents ev, hipStream_t s) {
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s, StageEvents ev) {
   if (a.rows_total == 0) return record_stage(ev, s);
-  const int64_t mean_rows = a.rows_total / (a.offsets ? a.n_groups + a.n_extra : 1);
+  if (a.offsets == nullptr) {
+    // One dense group (the shared experts as one FFN): the largest tile whose
+    // grid still gives most CUs a tile.  A decode-sized batch would leave the
+    // big tiles to a few workgroups that each stream megabytes of weights
+    // alone; it takes the 32-row streaming tiles below instead.
+    const int64_t nt = (a.N + (a.mode == kGateUp ? 127 : 255)) / (a.mode == kGateUp ? 128 : 256);
+    if (a.rows_total >= 192 && (a.rows_total + 255) / 256 * nt >= 256)
+      return launch_both<256, 256, 2, 4, 64, 2>(a, s, ev);
+    if (a.rows_total >= 64 && (a.rows_total + 127) / 128 * nt >= 128)
+      return launch_both<128, 256, 2, 2, 64, 2>(a, s, ev);
+    if (a.mode == kDown) return launch_cfg<32, 64, 1, 2, 64, 4, kDown>(a, s, ev);
+    return launch_cfg<32, 256, 1, 4, 64, 2, kGateUp>(a, s, ev);
+  }
+  const int64_t mean_rows = a.rows_total / (a.n_groups + a.n_extra);
   if (mean_rows >= 192) return launch_both<256, 256, 2, 4, 64, 2>(a, s, ev);
   if (mean_rows >= 64) return launch_both<128, 256, 2, 2, 64, 2>(a, s, ev);
   // Few rows per group: the weights stream through and every workgroup's
