@@ -218,8 +218,11 @@ int moe_route_stats(const moe_layer* layer, int64_t T, const void* x, const floa
  * sum_i G(x)_i E_i(x) and E_i is not evaluated where G(x)_i is zero, so each
  * expert needs the list of tokens whose gate for it is non-zero; the
  * DeepSeekMoE page, section 3.2, eq. 10, fixes K' such experts per token.
- *   topk_idx [T, K'] with 0 <= id < N_r and distinct ids per token (other
- *   input is undefined behaviour), x [T, d] (dtype)
+ *   topk_idx [T, K'] with 0 <= id < N_r and distinct ids per token, x [T, d]
+ *   (dtype).  Other ids are undefined behaviour in libmoe.so; the checked
+ *   build libmoe_debug.so (MOE_DEBUG) verifies them on the device first and
+ *   returns MOE_ERR_INVALID_ARG with no output written, waiting for the
+ *   stream to read the result (the one call that synchronises there).
  *   -> counts [N_r], offsets [N_r + 1] (exclusive scan, offsets[N_r] = P),
  *      row_token [P] (token of each row), slot_row [P] (row of slot t*K'+j),
  *      x_perm [P, d] (x_perm[r] = x[row_token[r]]; NULL skips the copy).

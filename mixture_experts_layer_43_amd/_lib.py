@@ -6,6 +6,8 @@ import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
+# The checked build (MOE_DEBUG): moe_permute verifies caller-supplied ids.
+DEBUG_LIB_PATH = os.path.join(_HERE, "libmoe_debug.so")
 
 (MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP,
  MOE_ERR_SCRATCH_TOO_SMALL) = range(6)
@@ -41,6 +43,7 @@ class MoeError(RuntimeError):
 
 
 _lib = None
+_lib_checked = None
 
 P = ctypes.c_void_p
 I64 = ctypes.c_int64
@@ -67,21 +70,33 @@ _SIGS = {
 }
 
 
+def _load(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing; build it with "
+                          "`python -m mixture_experts_layer_43_amd.build`")
+    h = ctypes.CDLL(path)
+    for name, (args, res) in _SIGS.items():
+        f = getattr(h, name)
+        f.argtypes, f.restype = args, res
+    return h
+
+
 def lib() -> ctypes.CDLL:
     """Load libmoe.so (built in-tree by mixture_experts_layer_43_amd.build).
 
     There is no fallback: a missing library is an error."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is missing; build it with "
-                              "`python -m mixture_experts_layer_43_amd.build`")
-        h = ctypes.CDLL(LIB_PATH)
-        for name, (args, res) in _SIGS.items():
-            f = getattr(h, name)
-            f.argtypes, f.restype = args, res
-        _lib = h
+        _lib = _load(LIB_PATH)
     return _lib
+
+
+def lib_checked() -> ctypes.CDLL:
+    """Load libmoe_debug.so, the checked build of the same library."""
+    global _lib_checked
+    if _lib_checked is None:
+        _lib_checked = _load(DEBUG_LIB_PATH)
+    return _lib_checked
 
 
 def status_str(status: int) -> str:

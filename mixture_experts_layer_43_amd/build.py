@@ -3,8 +3,11 @@
     python -m mixture_experts_layer_43_amd.build
 
 Each .hip under csrc/ is compiled separately (in parallel) and linked into
-mixture_experts_layer_43_amd/libmoe.so.  Object files go to _build/ at the
-repository root.
+mixture_experts_layer_43_amd/libmoe.so.  The checked library
+libmoe_debug.so is linked from the same objects except the C-ABI layer,
+which is compiled again with MOE_DEBUG (moe_permute then verifies
+caller-supplied expert ids before using them).  Object files go to _build/ at
+the repository root.
 """
 from __future__ import annotations
 
@@ -20,7 +23,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
+DEBUG_LIB = os.path.join(PKG, "libmoe_debug.so")
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
+# The one source whose code differs in the checked build.
+DEBUG_SOURCE = "api.hip"
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
@@ -36,21 +42,19 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+def _compile(job) -> str:
+    src, debug = job
+    out_dir = os.path.join(BUILD, "debug") if debug else BUILD
+    obj = os.path.join(out_dir, os.path.basename(src)[:-4] + ".o")
+    cmd = [HIPCC, *CFLAGS, *(["-DMOE_DEBUG"] if debug else []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    with ThreadPoolExecutor(max(1, min(len(srcs), os.cpu_count() or 1))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -59,10 +63,25 @@ def build(verbose: bool = False) -> str:
     nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
     missing = [l.split()[-1] for l in nm.stdout.splitlines() if "device_stub" in l]
     if missing:
-        raise RuntimeError("kernel host stubs missing from libmoe.so:\n" + "\n".join(missing))
-    os.replace(tmp, LIB)
+        raise RuntimeError("kernel host stubs missing from " + os.path.basename(lib) + ":\n" +
+                           "\n".join(missing))
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(os.path.join(BUILD, "debug"), exist_ok=True)
+    srcs = sources()
+    dbg_src = os.path.join(CSRC, DEBUG_SOURCE)
+    jobs = [(s, False) for s in srcs] + [(dbg_src, True)]
+    with ThreadPoolExecutor(max(1, min(len(jobs), os.cpu_count() or 1))) as ex:
+        objs = list(ex.map(_compile, jobs))
+    release, dbg_obj = objs[:-1], objs[-1]
+    _link(release, LIB)
+    _link([dbg_obj if os.path.basename(o) == DEBUG_SOURCE[:-4] + ".o" else o for o in release],
+          DEBUG_LIB)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources", file=sys.stderr)
+        print(f"built {LIB} and {os.path.basename(DEBUG_LIB)} from {len(srcs)} sources",
+              file=sys.stderr)
     return LIB
 
 

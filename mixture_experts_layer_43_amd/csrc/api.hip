@@ -504,6 +504,20 @@ int moe_permute(const moe_layer* layer, int64_t T, const int32_t* topk_idx, cons
   MOE_TRY(need(ws));
   const Layout lo = layout_of(layer, T);
   if (ws_bytes < lo.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+#ifdef MOE_DEBUG
+  // Checked build: the caller's ids are verified on the device before the
+  // dispatch indexes with them (the flag sits in the block-local rank
+  // scratch, which the dispatch overwrites later); this waits for the stream.
+  if (T > 0) {
+    int32_t* bad = reinterpret_cast<int32_t*>(at(ws, lo.local_rank));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    MOE_HIP(moe::launch_check_topk(topk_idx, static_cast<int>(T), layer->top_k, layer->n_routed, bad, s));
+    int32_t h = 0;
+    MOE_HIP(hipMemcpyAsync(&h, bad, sizeof(h), hipMemcpyDeviceToHost, s));
+    MOE_HIP(hipStreamSynchronize(s));
+    if (h != 0) return MOE_ERR_INVALID_ARG;
+  }
+#endif
   return permute_impl(layer, T, topk_idx, x, counts, offsets, row_token, slot_row, x_perm, ws,
                       lo, static_cast<hipStream_t>(stream));
 }

@@ -352,6 +352,32 @@ hipError_t launch_dropless(const PermuteArgs& a, hipStream_t s) {
 
 }  // namespace
 
+// Caller-supplied routing checked before a dispatch uses it: one thread per
+// token sets *bad when an id lies outside [0, N_r) or repeats within the
+// token's K' ids.  Reads topk_idx only.
+__global__ __launch_bounds__(256) void check_topk_kernel(const int32_t* __restrict__ topk_idx, int T,
+                                                         int K, int Nr, int32_t* __restrict__ bad) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  int32_t id[16];
+  bool ok = true;
+  for (int j = 0; j < K; ++j) {
+    id[j] = topk_idx[static_cast<int64_t>(t) * K + j];
+    ok = ok && id[j] >= 0 && id[j] < Nr;
+    for (int i = 0; i < j; ++i) ok = ok && id[i] != id[j];
+  }
+  if (!ok) *bad = 1;
+}
+
+hipError_t launch_check_topk(const int32_t* topk_idx, int T, int K, int Nr, int32_t* bad,
+                             hipStream_t s) {
+  hipError_t err = launch_zero(bad, sizeof(int32_t), s);
+  if (err != hipSuccess || T == 0) return err;
+  hipLaunchKernelGGL(check_topk_kernel, dim3(static_cast<unsigned>((T + 255) / 256)), dim3(256), 0, s,
+                     topk_idx, T, K, Nr, bad);
+  return hipGetLastError();
+}
+
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s) {
   if (a.T == 0) {
     // Empty batch: all counts and offsets are zero.

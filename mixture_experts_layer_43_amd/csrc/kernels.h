@@ -69,6 +69,10 @@ struct PermuteArgs {
   int32_t* group_base;      // ws: [N_r, n_groups]
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+// *bad = 0, then 1 if any token's K' <= 16 ids leave [0, Nr) or repeat
+// (the checked build's moe_permute).
+hipError_t launch_check_topk(const int32_t* topk_idx, int T, int K, int Nr, int32_t* bad,
+                             hipStream_t s);
 
 
 // ---- grouped GEMMs (gemm_bf16.hip, gemm_f32.hip) ----

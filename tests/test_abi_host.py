@@ -29,6 +29,18 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(_lib.EXPORTS)
 
 
+def test_checked_library_exports_the_same_functions():
+    """libmoe_debug.so (MOE_DEBUG: moe_permute verifies caller-supplied ids)
+    loads beside libmoe.so and exports the same calls."""
+    C = _lib.lib_checked()
+    for n in declared_functions():
+        assert hasattr(C, n), n
+    assert C.moe_abi_version() == _lib.lib().moe_abi_version()
+    st, _ = ws_size(layer(), 8)
+    sz = ctypes.c_size_t(0)
+    assert C.moe_workspace_size(ctypes.byref(layer()), 8, ctypes.byref(sz)) == st
+
+
 def test_version_and_status_strings():
     L = _lib.lib()
     assert L.moe_abi_version() == 3
