@@ -6,8 +6,10 @@ Each .hip under csrc/ is compiled separately (in parallel) and linked into
 mixture_experts_layer_43_amd/libmoe.so.  The checked library
 libmoe_debug.so is linked from the same objects except the C-ABI layer,
 which is compiled again with MOE_DEBUG (moe_permute then verifies
-caller-supplied expert ids before using them).  Object files go to _build/ at
-the repository root.
+caller-supplied expert ids before using them), and libmoe_asan.so likewise
+with the host side of that layer under AddressSanitizer (for the host tests;
+it needs the sanitizer runtime preloaded).  Object files go to _build/ at the
+repository root.
 """
 from __future__ import annotations
 
@@ -24,8 +26,13 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 DEBUG_LIB = os.path.join(PKG, "libmoe_debug.so")
+# Host-side AddressSanitizer build of the C-ABI layer (argument checks,
+# workspace layout); the device code is not instrumented.
+ASAN_LIB = os.path.join(PKG, "libmoe_asan.so")
+ASAN_HOST = "-Xarch_host -fsanitize=address -Xarch_host -fno-omit-frame-pointer".split()
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
-# The one source whose code differs in the checked build.
+# The C-ABI layer: the one source compiled again for the checked and
+# sanitizer builds.
 DEBUG_SOURCE = "api.hip"
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -43,19 +50,20 @@ def sources():
 
 
 def _compile(job) -> str:
-    src, debug = job
-    out_dir = os.path.join(BUILD, "debug") if debug else BUILD
+    src, variant = job
+    out_dir = os.path.join(BUILD, variant) if variant else BUILD
     obj = os.path.join(out_dir, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *CFLAGS, *(["-DMOE_DEBUG"] if debug else []), "-c", src, "-o", obj]
+    extra = {"": [], "debug": ["-DMOE_DEBUG"], "asan": ["-g", *ASAN_HOST]}[variant]
+    cmd = [HIPCC, *CFLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def _link(objs, lib):
+def _link(objs, lib, extra=()):
     tmp = lib + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
@@ -69,19 +77,22 @@ def _link(objs, lib):
 
 
 def build(verbose: bool = False) -> str:
-    os.makedirs(os.path.join(BUILD, "debug"), exist_ok=True)
+    for v in ("debug", "asan"):
+        os.makedirs(os.path.join(BUILD, v), exist_ok=True)
     srcs = sources()
-    dbg_src = os.path.join(CSRC, DEBUG_SOURCE)
-    jobs = [(s, False) for s in srcs] + [(dbg_src, True)]
+    api_src = os.path.join(CSRC, DEBUG_SOURCE)
+    jobs = [(s, "") for s in srcs] + [(api_src, "debug"), (api_src, "asan")]
     with ThreadPoolExecutor(max(1, min(len(jobs), os.cpu_count() or 1))) as ex:
         objs = list(ex.map(_compile, jobs))
-    release, dbg_obj = objs[:-1], objs[-1]
+    release, dbg_obj, asan_obj = objs[:-2], objs[-2], objs[-1]
+    api_obj = DEBUG_SOURCE[:-4] + ".o"
+    swap = lambda o: [o if os.path.basename(r) == api_obj else r for r in release]
     _link(release, LIB)
-    _link([dbg_obj if os.path.basename(o) == DEBUG_SOURCE[:-4] + ".o" else o for o in release],
-          DEBUG_LIB)
+    _link(swap(dbg_obj), DEBUG_LIB)
+    _link(swap(asan_obj), ASAN_LIB, ASAN_HOST[:2])
     if verbose:
-        print(f"built {LIB} and {os.path.basename(DEBUG_LIB)} from {len(srcs)} sources",
-              file=sys.stderr)
+        print(f"built {LIB}, {os.path.basename(DEBUG_LIB)} and {os.path.basename(ASAN_LIB)} "
+              f"from {len(srcs)} sources", file=sys.stderr)
     return LIB
 
 
