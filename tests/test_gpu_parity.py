@@ -55,6 +55,11 @@ MID = {
     # expert, so the 32-row tiles.
     "mid-ragged-k-small": LayerConfig(name="mid-ragged-k-small", tokens=64, d_model=40, n_routed=32,
                                       n_shared=1, top_k=4, d_ff=16, d_ff_shared=48, seed=112),
+    # fp32 layer with several 64-row tiles per expert, a folded shared
+    # expert and K (d = 200, I = 100) that leaves a partial last step of 32.
+    "mid-f32-ragged": LayerConfig(name="mid-f32-ragged", tokens=700, d_model=200, n_routed=8,
+                                  n_shared=1, top_k=2, d_ff=100, d_ff_shared=100, dtype="f32",
+                                  seed=114),
     # Decode-sized batch of a 16B-like layer with d = 2040 and I = 1392.
     "decode-ragged-k": LayerConfig(name="decode-ragged-k", tokens=128, d_model=2040, n_routed=64,
                                    n_shared=2, top_k=6, d_ff=1392, d_ff_shared=1392, seed=113),
@@ -163,7 +168,7 @@ def ref_rows(cfg, inp, ref):
 
 
 @pytest.mark.parametrize("name", ["tiny-f32", "mid-ragged", "mid-smallm", "mid-medm", "mid-f32",
-                                  *RAGGED_K])
+                                  "mid-f32-ragged", *RAGGED_K])
 def test_expert_ffn_alone(name):
     cfg, inp, ref = case(name)
     announce(f"expert_ffn {name}")
@@ -178,7 +183,7 @@ def test_expert_ffn_alone(name):
 
 
 @pytest.mark.parametrize("name", ["tiny-f32", "mid-ragged", "mid-smallm", "mid-f32", "mid-medm",
-                                  *RAGGED_K])
+                                  "mid-f32-ragged", *RAGGED_K])
 def test_shared_ffn_alone(name):
     cfg, inp, ref = case(name)
     announce(f"shared_ffn {name}")
