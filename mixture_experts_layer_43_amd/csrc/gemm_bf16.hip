@@ -748,6 +748,12 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s, StageEvents ev) {
   const int64_t mean_rows = a.rows_total / (a.n_groups + a.n_extra);
   if (mean_rows >= 192) return launch_both<256, 256, 2, 4, 64, 2>(a, s, ev);
   if (mean_rows >= 64) return launch_both<128, 256, 2, 2, 64, 2>(a, s, ev);
+  // 33-63 rows per group: one 64-row tile per group, where 32-row tiles
+  // would take two per group and each would stream the group's weights.
+  if (mean_rows > 32) {
+    if (a.mode == kDown) return launch_cfg<64, 128, 2, 2, 64, 4, kDown>(a, s, ev);
+    return launch_cfg<64, 256, 1, 4, 64, 2, kGateUp>(a, s, ev);
+  }
   // Few rows per group: the weights stream through and every workgroup's
   // time is its share of them.  Narrow down tiles (64 columns) split the
   // stream finer, so the last partial round of workgroups is short; four
