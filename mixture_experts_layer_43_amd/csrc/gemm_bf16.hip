@@ -741,18 +741,21 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s, StageEvents ev) {
     if (a.rows_total >= 192 && (a.rows_total + 255) / 256 * nt >= 256)
       return launch_both<256, 256, 2, 4, 64, 2>(a, s, ev);
     if (a.rows_total >= 64 && (a.rows_total + 127) / 128 * nt >= 128)
-      return launch_both<128, 256, 2, 2, 64, 2>(a, s, ev);
+      return launch_both<128, 256, 2, 2, 64, 3>(a, s, ev);
     if (a.mode == kDown) return launch_cfg<32, 64, 1, 2, 64, 4, kDown>(a, s, ev);
     return launch_cfg<32, 256, 1, 4, 64, 2, kGateUp>(a, s, ev);
   }
   const int64_t mean_rows = a.rows_total / (a.n_groups + a.n_extra);
   if (mean_rows >= 192) return launch_both<256, 256, 2, 4, 64, 2>(a, s, ev);
-  if (mean_rows >= 64) return launch_both<128, 256, 2, 2, 64, 2>(a, s, ev);
+  // Below 192 rows per group the weights dominate the traffic; three LDS
+  // stages keep two K steps of copies in flight (144 KB and 120 / 72 KB of
+  // LDS per workgroup).
+  if (mean_rows >= 64) return launch_both<128, 256, 2, 2, 64, 3>(a, s, ev);
   // 33-63 rows per group: one 64-row tile per group, where 32-row tiles
   // would take two per group and each would stream the group's weights.
   if (mean_rows > 32) {
-    if (a.mode == kDown) return launch_cfg<64, 128, 2, 2, 64, 4, kDown>(a, s, ev);
-    return launch_cfg<64, 256, 1, 4, 64, 2, kGateUp>(a, s, ev);
+    if (a.mode == kDown) return launch_cfg<64, 128, 2, 2, 64, 3, kDown>(a, s, ev);
+    return launch_cfg<64, 256, 1, 4, 64, 3, kGateUp>(a, s, ev);
   }
   // Few rows per group: the weights stream through and every workgroup's
   // time is its share of them.  Narrow down tiles (64 columns) split the
