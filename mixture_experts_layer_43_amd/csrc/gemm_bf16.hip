@@ -31,6 +31,11 @@ namespace {
 
 constexpr int kXcds = 8;
 constexpr int kPanel = 8;   // row tiles per panel in the grouped tile order
+// Cache policy of the weight (B) copies for tiles whose expert groups mostly
+// fit in one row tile: the non-temporal hint (aux bit 1).  Each weight byte is
+// then read once, and streaming it past the caches leaves them to the
+// activations that are read again.
+constexpr int kStreamB = 2;
 
 // Buffer resource over `bytes` bytes at `base` (raw buffer: offsets are byte
 // offsets; loads past `bytes` return zero instead of faulting).
@@ -131,7 +136,7 @@ __device__ __forceinline__ void lds_barrier() {
 // stage `s`: A_LD loads for A rows and B_LD for B rows per wavefront, each
 // 64 lanes x 16 B = 1 KB of LDS (64/(BK/8) tile rows).  Per-lane byte
 // offsets are fixed over K; the K position goes in the scalar offset.
-template <int BM, int BK, int A_LD, int B_LD>
+template <int BM, int BK, int A_LD, int B_LD, int BPOL>
 __device__ __forceinline__ void copy_step(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                           const uint32_t (&a_off)[A_LD], const uint32_t (&b_off)[B_LD],
                                           int k, int k_sub, int64_t b_sub_stride, bool packed,
@@ -152,7 +157,7 @@ __device__ __forceinline__ void copy_step(__amdgpu_buffer_rsrc_t ra, __amdgpu_bu
 #pragma unroll
   for (int i = 0; i < B_LD; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, lds_ptr(s + BM * BK + (wv * B_LD + i) * R * BK), 16,
-                                             b_off[i], sb, 0, 0);
+                                             b_off[i], sb, 0, BPOL);
 }
 
 // Ragged K: the K of one sub-matrix (k_sub) is a multiple of 8 but not of
@@ -162,7 +167,7 @@ __device__ __forceinline__ void copy_step(__amdgpu_buffer_rsrc_t ra, __amdgpu_bu
 // of B.  A lane whose 16-byte chunk lies past kvalid copies its row's first
 // chunk of the step instead, so every address stays inside the row; the B
 // fragments of those chunks are zeroed before the MFMAs (mask_b).
-template <int BM, int BK, int A_LD, int B_LD>
+template <int BM, int BK, int A_LD, int B_LD, int BPOL>
 __device__ __forceinline__ void copy_step_ragged(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                                  const uint32_t (&a_off)[A_LD],
                                                  const uint32_t (&b_off)[B_LD], int kt, int sps,
@@ -186,7 +191,7 @@ __device__ __forceinline__ void copy_step_ragged(__amdgpu_buffer_rsrc_t ra, __am
     const int c = lp ^ swz<BK>((wv * B_LD + i) * R + lr);
     const uint32_t o = c * 8 < kvalid ? b_off[i] : b_off[i] - static_cast<uint32_t>(c * 16);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, lds_ptr(s + BM * BK + (wv * B_LD + i) * R * BK), 16, o,
-                                             sb, 0, 0);
+                                             sb, 0, BPOL);
   }
 }
 
@@ -281,7 +286,7 @@ __device__ __forceinline__ void step_body(f32x16 (&acc)[MB][NB], Frags<MB, NB>& 
 // any more), issues the copy of step kt+STAGES-1 into that stage and
 // computes.  A wavefront whose rows are all past the tile's last row
 // (MBA == 0) only copies and waits.
-template <int BM, int BK, int STAGES, int MB, int NB, int MBA, int A_LD, int B_LD, bool RAGGED>
+template <int BM, int BK, int STAGES, int MB, int NB, int MBA, int A_LD, int B_LD, bool RAGGED, int BPOL>
 __device__ __forceinline__ void k_loop(f32x16 (&acc)[MB][NB], __amdgpu_buffer_rsrc_t ra,
                                        __amdgpu_buffer_rsrc_t rb, const uint32_t (&a_off)[A_LD],
                                        const uint32_t (&b_off)[B_LD], int nk, int k_sub,
@@ -297,10 +302,10 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[MB][NB], __amdgpu_buffer_rs
     const int kn = kt + STAGES - 1;
     if (kn < nk) {
       if constexpr (RAGGED)
-        copy_step_ragged<BM, BK, A_LD, B_LD>(ra, rb, a_off, b_off, kn, sps, k_sub, kstride_b, wv, lane,
+        copy_step_ragged<BM, BK, A_LD, B_LD, BPOL>(ra, rb, a_off, b_off, kn, sps, k_sub, kstride_b, wv, lane,
                                              smem + (kn % STAGES) * se);
       else
-        copy_step<BM, BK, A_LD, B_LD>(ra, rb, a_off, b_off, kn * BK, k_sub, kstride_b, packed, wv,
+        copy_step<BM, BK, A_LD, B_LD, BPOL>(ra, rb, a_off, b_off, kn * BK, k_sub, kstride_b, packed, wv,
                                       smem + (kn % STAGES) * se);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -315,7 +320,7 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[MB][NB], __amdgpu_buffer_rs
 
 // GROUPED: rows come in per-expert groups described by offsets (routed
 // experts); otherwise one dense group (shared experts).
-template <int BM, int BN, int WM, int WN, int BK, int STAGES, int MODE, bool GROUPED, bool RAGGED>
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int MODE, bool GROUPED, bool RAGGED, int BPOL>
 __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr int TM = BM / WM;               // rows per wavefront
@@ -514,17 +519,17 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
   for (int j = 0; j < STAGES - 1; ++j) {
     if (j < nk) {
       if constexpr (RAGGED)
-        copy_step_ragged<BM, BK, A_LD, B_LD>(ra, rb, a_off, b_off, j, sps, p.k_sub, kstride_b, wv, lane,
+        copy_step_ragged<BM, BK, A_LD, B_LD, BPOL>(ra, rb, a_off, b_off, j, sps, p.k_sub, kstride_b, wv, lane,
                                              smem + j * SE);
       else
-        copy_step<BM, BK, A_LD, B_LD>(ra, rb, a_off, b_off, j * BK, p.k_sub, kstride_b, p.packed, wv,
+        copy_step<BM, BK, A_LD, B_LD, BPOL>(ra, rb, a_off, b_off, j * BK, p.k_sub, kstride_b, p.packed, wv,
                                       smem + j * SE);
     }
   }
   // 32-row blocks of this wavefront that hold rows of the tile.
   const int mba = __builtin_amdgcn_readfirstlane(max(0, min(MB, (rows - wm * TM + 31) / 32)));
 #define MOE_K_LOOP(n)                                                                            \
-  k_loop<BM, BK, STAGES, MB, NB, n, A_LD, B_LD, RAGGED>(acc, ra, rb, a_off, b_off, nk, p.k_sub,   \
+  k_loop<BM, BK, STAGES, MB, NB, n, A_LD, B_LD, RAGGED, BPOL>(acc, ra, rb, a_off, b_off, nk, p.k_sub, \
                                                         kstride_b, p.packed, wv, khalf, a_row,     \
                                                         b_row, smem, SE, sps, lane)
   if (mba == MB) {
@@ -657,7 +662,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
 #endif
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int STAGES, int MODE>
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int MODE, int BPOL = 0>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t s, StageEvents ev) {
   static_assert(BK == 32 || BK == 64, "K steps divide the packed layout's 64-wide steps");
   constexpr int OUT_N = (MODE == kGateUp) ? BN / 2 : BN;
@@ -678,7 +683,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s, StageEvents ev) {
   const bool ragged = a.k_sub % BK != 0;
   if (ragged && a.packed) return hipErrorInvalidValue;
 #define MOE_GEMM_LAUNCH(G, R)                                                                        \
-  hipExtLaunchKernelGGL((grouped_gemm_bf16<BM, BN, WM, WN, BK, STAGES, MODE, G, R>), dim3(grid), block, 0, \
+  hipExtLaunchKernelGGL((grouped_gemm_bf16<BM, BN, WM, WN, BK, STAGES, MODE, G, R, BPOL>), dim3(grid), block, 0, \
                         s, ev.start, ev.stop, 0, a)
   if (a.offsets != nullptr) {
     if (ragged) MOE_GEMM_LAUNCH(true, true);
@@ -691,10 +696,10 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s, StageEvents ev) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int STAGES>
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int BPOL = 0>
 hipError_t launch_both(const GemmArgs& a, hipStream_t s, StageEvents ev) {
-  return a.mode == kGateUp ? launch_cfg<BM, BN, WM, WN, BK, STAGES, kGateUp>(a, s, ev)
-                           : launch_cfg<BM, BN, WM, WN, BK, STAGES, kDown>(a, s, ev);
+  return a.mode == kGateUp ? launch_cfg<BM, BN, WM, WN, BK, STAGES, kGateUp, BPOL>(a, s, ev)
+                           : launch_cfg<BM, BN, WM, WN, BK, STAGES, kDown, BPOL>(a, s, ev);
 }
 
 // One 16-byte chunk (8 consecutive k of one row) per thread.
@@ -746,24 +751,36 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s, StageEvents ev) {
     return launch_cfg<32, 256, 1, 4, 64, 2, kGateUp>(a, s, ev);
   }
   const int64_t mean_rows = a.rows_total / (a.n_groups + a.n_extra);
-  if (mean_rows >= 192) return launch_both<256, 256, 2, 4, 64, 2>(a, s, ev);
-  // Below 192 rows per group the weights dominate the traffic; three LDS
-  // stages keep two K steps of copies in flight (144 KB and 120 / 72 KB of
-  // LDS per workgroup).
-  if (mean_rows >= 64) return launch_both<128, 256, 2, 2, 64, 3>(a, s, ev);
-  // 33-63 rows per group: one 64-row tile per group, where 32-row tiles
-  // would take two per group and each would stream the group's weights.
-  if (mean_rows > 32) {
-    if (a.mode == kDown) return launch_cfg<64, 128, 2, 2, 64, 3, kDown>(a, s, ev);
-    return launch_cfg<64, 256, 1, 4, 64, 3, kGateUp>(a, s, ev);
+  // Tiles by mean rows per group, from sweeps of the 16B-shaped layer's
+  // GEMMs over batch sizes with the routing's real spread of group sizes and
+  // the T-row shared groups.  256-row tiles from 160 rows: at 171 and 186
+  // rows they take 213 and 224 us for gate/up where 128-row tiles, needing
+  // two row tiles for many groups, take 249 and 278 us; at 155 rows it is
+  // 221 against 182 us the other way.
+  if (mean_rows >= 160) return launch_both<256, 256, 2, 4, 64, 2>(a, s, ev);
+  // Below that most groups fit in one row tile, so each weight byte is read
+  // once: the weight copies go non-temporal (gate/up 4-6 us and down 2-5 us
+  // less at 93-155 rows; with 256-row tiles at 16k tokens they would cost
+  // 2-3 %, as weight tiles are read by several row tiles there).  Three
+  // stages keep two K steps of copies in flight (144 KB of LDS).
+  if (mean_rows >= 64) return launch_both<128, 256, 2, 2, 64, 3, kStreamB>(a, s, ev);
+  // 17-63 rows: one 64-row tile per group, where 32-row tiles would take two
+  // per group and each would stream the group's weights.  Gate/up 64x256
+  // with two stages (80 KB: two workgroups per CU) beats three stages (one
+  // workgroup per CU) by 8-20 % with real group sizes (e.g. 122 against 142
+  // us at 31 rows, 140 against 148 us at 62 rows).
+  if (mean_rows > 16) {
+    if (a.mode == kDown) return launch_cfg<64, 128, 2, 2, 64, 3, kDown, kStreamB>(a, s, ev);
+    return launch_cfg<64, 256, 1, 4, 64, 2, kGateUp, kStreamB>(a, s, ev);
   }
-  // Few rows per group: the weights stream through and every workgroup's
-  // time is its share of them.  Narrow down tiles (64 columns) split the
-  // stream finer, so the last partial round of workgroups is short; four
-  // stages keep three K steps of copies in flight (48 KB of LDS, three
-  // workgroups per CU: about 110 KB in flight per CU instead of 72 KB).
-  if (a.mode == kDown) return launch_cfg<32, 64, 1, 2, 64, 4, kDown>(a, s, ev);
-  return launch_cfg<32, 256, 1, 4, 64, 2, kGateUp>(a, s, ev);
+  // Few rows per group (the decode shape): the weights stream through and
+  // every workgroup's time is its share of them.  Narrow down tiles (64
+  // columns) split the stream finer, so the last partial round of
+  // workgroups is short; four stages keep three K steps of copies in flight
+  // (48 KB of LDS, three workgroups per CU).  Non-temporal weight copies:
+  // gate/up 140 -> 120 us and down 72 -> 64 us at 16 rows per group.
+  if (a.mode == kDown) return launch_cfg<32, 64, 1, 2, 64, 4, kDown, kStreamB>(a, s, ev);
+  return launch_cfg<32, 256, 1, 4, 64, 2, kGateUp, kStreamB>(a, s, ev);
 }
 
 }  // namespace moe
