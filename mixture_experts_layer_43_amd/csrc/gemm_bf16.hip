@@ -13,13 +13,16 @@
 // wavefront holds matching gate and up accumulators and applies
 // silu(gate) * up in registers before the single bf16 store of H.  Down mode
 // is a plain A . B^T.  Operands go global -> LDS directly
-// (global_load_lds_dwordx4, no staging registers; two stages; 16-byte chunks
-// in XOR-swizzled rows so the 16-byte fragment reads of a quarter-wave hit
-// distinct banks) -> v_mfma_f32_32x32x16_bf16 with fp32 accumulation.
-// Workgroup ids are remapped so that consecutive tiles run on the same XCD
-// and share its L2.  A K that is a multiple of 8 but not of BK takes a
-// separate instantiation (RAGGED) whose last step per weight matrix is
-// partial; the aligned instantiation does not carry its checks.
+// (global_load_lds_dwordx4, no staging registers; two to four stages;
+// 16-byte chunks in XOR-swizzled rows so the 16-byte fragment reads of a
+// quarter-wave hit distinct banks) -> v_mfma_f32_32x32x16_bf16 with fp32
+// accumulation.  Workgroup ids are remapped so that consecutive tiles run on
+// the same XCD and share its L2.  A K that is a multiple of 8 but not of BK
+// takes a separate instantiation (RAGGED) whose last step per weight matrix
+// is partial; the aligned instantiation does not carry its checks.  The
+// tile configuration and the weight copies' cache policy follow the mean
+// rows per group (launch_gemm_bf16); every configuration sums each output
+// over K in the same order, so the choice changes no result.
 #include "common.h"
 #include <hip/hip_ext.h>
 
