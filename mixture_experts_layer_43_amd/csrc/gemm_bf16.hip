@@ -26,6 +26,8 @@
 #include "common.h"
 #include <hip/hip_ext.h>
 
+#include <cmath>
+
 #include "kernels.h"
 
 namespace moe {
@@ -738,6 +740,25 @@ hipError_t record_stage(StageEvents ev, hipStream_t s) {
   return ev.stop != nullptr ? hipEventRecord(ev.stop, s) : hipSuccess;
 }
 
+// Expected number of row tiles of height h for a group whose size is
+// Poisson with mean mu: the sum over j >= 0 of P(size > j h), each tail from
+// the normal approximation with a continuity correction.
+static double expected_row_tiles(double mu, int h) {
+  if (mu <= 0.0) return 0.0;
+  const double sd = std::sqrt(mu);
+  double e = 0.0;
+  for (int j = 0; j * static_cast<double>(h) <= mu + 8.0 * sd; ++j)
+    e += 0.5 * std::erfc((j * static_cast<double>(h) + 0.5 - mu) / (sd * std::sqrt(2.0)));
+  return e;
+}
+
+// Time per row of a full row tile relative to the 256x256 tile, measured on
+// the 16B-shaped layer's GEMMs where all three fit the groups exactly (8k
+// and 16k tokens: 192-row tiles 1.07-1.13, 128-row tiles 1.32-1.38); with
+// these weights the choice above picks the fastest tile at all eleven batch
+// sizes from 1k to 16k tokens measured (1536-1792 and 3072 tokens: 192 rows).
+static double tile_row_cost(int h) { return h == 256 ? 1.0 : h == 192 ? 1.14 : 1.30; }
+
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s, StageEvents ev) {
   if (a.rows_total == 0) return record_stage(ev, s);
   if (a.offsets == nullptr) {
@@ -754,19 +775,40 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s, StageEvents ev) {
     return launch_cfg<32, 256, 1, 4, 64, 2, kGateUp>(a, s, ev);
   }
   const int64_t mean_rows = a.rows_total / (a.n_groups + a.n_extra);
-  // Tiles by mean rows per group, from sweeps of the 16B-shaped layer's
-  // GEMMs over batch sizes with the routing's real spread of group sizes and
-  // the T-row shared groups.  256-row tiles from 160 rows: at 171 and 186
-  // rows they take 213 and 224 us for gate/up where 128-row tiles, needing
-  // two row tiles for many groups, take 249 and 278 us; at 155 rows it is
-  // 221 against 182 us the other way.
-  if (mean_rows >= 160) return launch_both<256, 256, 2, 4, 64, 2>(a, s, ev);
-  // Below that most groups fit in one row tile, so each weight byte is read
-  // once: the weight copies go non-temporal (gate/up 4-6 us and down 2-5 us
-  // less at 93-155 rows; with 256-row tiles at 16k tokens they would cost
-  // 2-3 %, as weight tiles are read by several row tiles there).  Three
-  // stages keep two K steps of copies in flight (144 KB of LDS).
-  if (mean_rows >= 64) return launch_both<128, 256, 2, 2, 64, 3, kStreamB>(a, s, ev);
+  if (mean_rows >= 64) {
+    // 128-, 192- or 256-row tiles, whichever leaves the least work: the
+    // expected row tiles of each height (routed groups: their sizes as a
+    // balanced router spreads them, Poisson around the mean; shared groups:
+    // exact) times the height times the tile's measured cost per row.
+    const double routed = static_cast<double>(a.rows_total) -
+                          static_cast<double>(a.n_extra) * static_cast<double>(a.extra_rows);
+    const double mu = routed / a.n_groups;
+    double best = 0.0;
+    int bm = 256;
+    // Past 4096 rows per group the last row tile's padding is a few % at
+    // most and 256-row tiles win.
+    for (const int h : {256, 192, 128}) {
+      if (h != 256 && mu > 4096.0) break;
+      const double tiles = a.n_groups * expected_row_tiles(mu, h) +
+                           static_cast<double>(a.n_extra) * ((a.extra_rows + h - 1) / h);
+      const double cost = tiles * h * tile_row_cost(h);
+      if (h == 256 || cost < best) {
+        best = cost;
+        bm = h;
+      }
+    }
+    // Where most groups fit in one row tile each weight byte is read once,
+    // and the weight copies go non-temporal; 256-row tiles keep plain
+    // copies (at 16k tokens the hint costs them 2-3 %, as a weight tile is
+    // read by several row tiles there).  Three stages for 128-row tiles keep
+    // two K steps of copies in flight (144 KB of LDS).
+    if (bm == 128) return launch_both<128, 256, 2, 2, 64, 3, kStreamB>(a, s, ev);
+    if (bm == 192) {
+      if (mu <= 192.0) return launch_both<192, 256, 2, 4, 64, 2, kStreamB>(a, s, ev);
+      return launch_both<192, 256, 2, 4, 64, 2>(a, s, ev);
+    }
+    return launch_both<256, 256, 2, 4, 64, 2>(a, s, ev);
+  }
   // 17-63 rows: one 64-row tile per group, where 32-row tiles would take two
   // per group and each would stream the group's weights.  Gate/up 64x256
   // with two stages (80 KB: two workgroups per CU) beats three stages (one

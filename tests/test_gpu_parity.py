@@ -65,9 +65,15 @@ MID = {
                               top_k=6, d_ff=192, d_ff_shared=192, seed=115),
     "mid-64rows-ragged": LayerConfig(name="mid-64rows-ragged", tokens=350, d_model=200, n_routed=32,
                                      n_shared=1, top_k=4, d_ff=176, d_ff_shared=176, seed=116),
-    # 64-159 rows per expert group: the 128-row tiles with ragged K.
+    # From 64 rows per expert group the launch weighs 128-, 192- and 256-row
+    # tiles: 128-row tiles here (75 and 88 routed rows per group, aligned and
+    # ragged K), 192-row tiles with plain weight copies below (300 rows).
     "mid-128rows-ragged": LayerConfig(name="mid-128rows-ragged", tokens=600, d_model=200, n_routed=16,
                                       n_shared=1, top_k=2, d_ff=176, d_ff_shared=176, seed=117),
+    "mid-128rows": LayerConfig(name="mid-128rows", tokens=700, d_model=256, n_routed=16, n_shared=1,
+                               top_k=2, d_ff=192, d_ff_shared=192, seed=118),
+    "mid-192rows": LayerConfig(name="mid-192rows", tokens=1200, d_model=256, n_routed=8, n_shared=0,
+                               top_k=2, d_ff=256, d_ff_shared=256, seed=119),
     # Decode-sized batch of a 16B-like layer with d = 2040 and I = 1392.
     "decode-ragged-k": LayerConfig(name="decode-ragged-k", tokens=128, d_model=2040, n_routed=64,
                                    n_shared=2, top_k=6, d_ff=1392, d_ff_shared=1392, seed=113),
@@ -177,7 +183,7 @@ def ref_rows(cfg, inp, ref):
 
 @pytest.mark.parametrize("name", ["tiny-f32", "mid-ragged", "mid-smallm", "mid-medm", "mid-f32",
                                   "mid-f32-ragged", "mid-64rows", "mid-64rows-ragged",
-                                  "mid-128rows-ragged", *RAGGED_K])
+                                  "mid-128rows-ragged", "mid-128rows", "mid-192rows", *RAGGED_K])
 def test_expert_ffn_alone(name):
     cfg, inp, ref = case(name)
     announce(f"expert_ffn {name}")

@@ -1,15 +1,17 @@
 """The expert GEMMs' tile configurations give the same bits.
 
-moe_expert_ffn picks its tiles from the mean rows per expert group: 256x256
-from 160 rows, 128x256 from 64, 64-row tiles from 17, 32-row tiles below,
-with non-temporal weight copies under 160 rows.  Every configuration sums
-each output over K in the same order (16-wide slices of 64-wide steps, in
-order, fp32 accumulation), so the choice must not change any result.  With
-every expert holding the same weights, cutting the same 4096 dispatched rows
-into 2 ... 256 groups moves the launch through every configuration while the
-FFN of each row stays the same (DeepSeekMoE page, section 3.2, eq. 9:
-FFN_i applied to the rows routed to expert i): y_perm must be bit-identical
-across the cuts, and within the bf16 tolerance of the oracle."""
+moe_expert_ffn picks its tiles from the rows per expert group: 32-row tiles
+up to 16 rows, 64-row tiles up to 63, and from 64 rows whichever of the
+128-, 192- and 256-row tiles leaves the least work for groups of that mean
+size, with non-temporal weight copies where the groups fit in one row tile.
+Every configuration sums each output over K in the same order (16-wide
+slices of 64-wide steps, in order, fp32 accumulation), so the choice must
+not change any result.  With every expert holding the same weights, cutting
+the same 4096 dispatched rows into 2 ... 256 groups moves the launch through
+every configuration while the FFN of each row stays the same (DeepSeekMoE
+page, section 3.2, eq. 9: FFN_i applied to the rows routed to expert i):
+y_perm must be bit-identical across the cuts, and within the bf16 tolerance
+of the oracle."""
 from __future__ import annotations
 
 import numpy as np
@@ -25,10 +27,10 @@ from test_gpu_parity import announce
 pytestmark = pytest.mark.gpu
 
 ROWS = 4096
-# Groups per cut; their mean rows (4096 // n) select 256x256 (2, 8, 25),
-# 128x256 (26, 40, 64), 64-row (65, 100, 200) and 32-row tiles (241, 256),
-# both sides of every boundary.
-CUTS = [2, 8, 25, 26, 40, 64, 65, 100, 200, 241, 256]
+# Groups per cut and the tiles their mean rows (4096 / n) select: 256 rows
+# (2, 8, 20), 192 rows with plain (14) and non-temporal copies (26), 128 rows
+# (34, 64), 64 rows (65, 100, 200) and 32 rows (241, 256).
+CUTS = [2, 8, 14, 20, 26, 34, 64, 65, 100, 200, 241, 256]
 
 
 def cut_offsets(n: int, seed: int) -> np.ndarray:
