@@ -752,12 +752,14 @@ static double expected_row_tiles(double mu, int h) {
   return e;
 }
 
-// Time per row of a full row tile relative to the 256x256 tile, measured on
-// the 16B-shaped layer's GEMMs where all three fit the groups exactly (8k
-// and 16k tokens: 192-row tiles 1.07-1.13, 128-row tiles 1.32-1.38); with
-// these weights the choice above picks the fastest tile at all eleven batch
-// sizes from 1k to 16k tokens measured (1536-1792 and 3072 tokens: 192 rows).
-static double tile_row_cost(int h) { return h == 256 ? 1.0 : h == 192 ? 1.14 : 1.30; }
+// Time per row of a row tile relative to the 256x256 tile.  Where all three fit
+// the groups exactly (the 16B-shaped layer's GEMMs at 8k and 16k tokens)
+// 192-row tiles take 1.07-1.13 and 128-row tiles 1.32-1.38; the weights are
+// fitted to the fastest tile of the whole layer with the router's own spread
+// of group sizes at 1k-3k tokens (128 rows at 1024 and 1152 tokens, 192 rows
+// at 1280-1792 and 3072) and of the GEMMs at 2k-16k tokens (256 rows): any
+// 128-row weight from 1.38 to 1.50 with 1.14 picks all thirteen.
+static double tile_row_cost(int h) { return h == 256 ? 1.0 : h == 192 ? 1.14 : 1.42; }
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s, StageEvents ev) {
   if (a.rows_total == 0) return record_stage(ev, s);

@@ -28,9 +28,9 @@ pytestmark = pytest.mark.gpu
 
 ROWS = 4096
 # Groups per cut and the tiles their mean rows (4096 / n) select: 256 rows
-# (2, 8, 20), 192 rows with plain (14) and non-temporal copies (26), 128 rows
-# (34, 64), 64 rows (65, 100, 200) and 32 rows (241, 256).
-CUTS = [2, 8, 14, 20, 26, 34, 64, 65, 100, 200, 241, 256]
+# (2, 8, 20), 192 rows with plain (14) and non-temporal copies (26, 34), 128
+# rows (40, 64), 64 rows (65, 100, 200) and 32 rows (241, 256).
+CUTS = [2, 8, 14, 20, 26, 34, 40, 64, 65, 100, 200, 241, 256]
 
 
 def cut_offsets(n: int, seed: int) -> np.ndarray:
