@@ -754,11 +754,13 @@ static double expected_row_tiles(double mu, int h) {
 
 // Time per row of a row tile relative to the 256x256 tile.  Where all three fit
 // the groups exactly (the 16B-shaped layer's GEMMs at 8k and 16k tokens)
-// 192-row tiles take 1.07-1.13 and 128-row tiles 1.32-1.38; the weights are
-// fitted to the fastest tile of the whole layer with the router's own spread
-// of group sizes at 1k-3k tokens (128 rows at 1024 and 1152 tokens, 192 rows
-// at 1280-1792 and 3072) and of the GEMMs at 2k-16k tokens (256 rows): any
-// 128-row weight from 1.38 to 1.50 with 1.14 picks all thirteen.
+// 192-row tiles take 1.07-1.13 and 128-row tiles 1.32-1.38.  The weights are
+// fitted to the fastest tile of each GEMM, every height forced in turn, with
+// the router's own spread of group sizes: the 16B-shaped layer at 1k-3k
+// tokens and the 2b-shaped layer (d = 1280, I = 896, 63 + 1 experts, top-7)
+// at 1k-4k tokens.  With the rounds counted below, 192-row weights from 1.10
+// to 1.18 and 128-row weights from 1.38 to 1.50 pick all 26 (gate/up and
+// down); without them 1.14 and 1.42 miss two of the 2b-shaped ones.
 static double tile_row_cost(int h) { return h == 256 ? 1.0 : h == 192 ? 1.14 : 1.42; }
 
 hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s, StageEvents ev) {
@@ -778,13 +780,25 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s, StageEvents ev) {
   }
   const int64_t mean_rows = a.rows_total / (a.n_groups + a.n_extra);
   if (mean_rows >= 64) {
-    // 128-, 192- or 256-row tiles, whichever leaves the least work: the
-    // expected row tiles of each height (routed groups: their sizes as a
-    // balanced router spreads them, Poisson around the mean; shared groups:
-    // exact) times the height times the tile's measured cost per row.
+    // 128-, 192- or 256-row tiles, whichever finishes first.  Every tile of
+    // one launch runs the same K loop, one workgroup per CU, so the launch
+    // takes ceil(tiles / CUs) rounds of tiles, each as long as the tile's
+    // height times its measured cost per row.  The row tiles are expected
+    // counts: routed groups with their sizes as a balanced router spreads
+    // them (Poisson around the mean), shared groups exactly; the column
+    // tiles follow N (128 output columns per gate/up tile, 256 per down
+    // tile).  Rounds matter where the grid is small: the 2b-shaped layer's
+    // gate/up at 1536 tokens makes 518 tiles of 192 rows (a third round of
+    // 6 tiles on 256 CUs) but 483 of 256 rows, and runs 81 against 103 us.
     const double routed = static_cast<double>(a.rows_total) -
                           static_cast<double>(a.n_extra) * static_cast<double>(a.extra_rows);
     const double mu = routed / a.n_groups;
+    const int out_cols = a.mode == kGateUp ? 128 : 256;
+    const double col_tiles = static_cast<double>((a.N + out_cols - 1) / out_cols);
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
     double best = 0.0;
     int bm = 256;
     // Past 4096 rows per group the last row tile's padding is a few % at
@@ -793,7 +807,8 @@ hipError_t launch_gemm_bf16(const GemmArgs& a, hipStream_t s, StageEvents ev) {
       if (h != 256 && mu > 4096.0) break;
       const double tiles = a.n_groups * expected_row_tiles(mu, h) +
                            static_cast<double>(a.n_extra) * ((a.extra_rows + h - 1) / h);
-      const double cost = tiles * h * tile_row_cost(h);
+      const double rounds = std::ceil(tiles * col_tiles / cus);
+      const double cost = rounds * h * tile_row_cost(h);
       if (h == 256 || cost < best) {
         best = cost;
         bm = h;
