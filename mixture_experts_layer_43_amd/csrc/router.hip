@@ -350,7 +350,7 @@ __device__ __forceinline__ void split3(float v, uint32_t& hi, uint32_t& mid, uin
   const float r1 = v - __uint_as_float(hi);
   mid = __float_as_uint(r1) & 0xFFFF0000u;
   const float r2 = r1 - __uint_as_float(mid);
-  lo = __float_as_uint(r2) & 0xFFFF0000u;
+  lo = __float_as_uint(r2);  // the pack below keeps the high half, as for hi and mid
 }
 
 // High halves of two fp32 patterns -> one packed bf16 pair (lo element first).
@@ -377,7 +377,7 @@ __device__ __forceinline__ void load_w_slice(float4 (&w)[NBLK][2], const float* 
 // consecutive MFMAs go to different accumulators.
 template <int MBLK, int NBLK>
 __device__ __forceinline__ void router_mma(f32x16 (&acc)[MBLK][NBLK], const bf16x8 (&a)[MBLK],
-                                           const float4 (&w)[NBLK][2], const bool (&ev)[NBLK]) {
+                                           const float4 (&w)[NBLK][2]) {
   bf16x8 bp[NBLK][3];
 #pragma unroll
   for (int nb = 0; nb < NBLK; ++nb) {
@@ -385,7 +385,7 @@ __device__ __forceinline__ void router_mma(f32x16 (&acc)[MBLK][NBLK], const bf16
                         w[nb][1].x, w[nb][1].y, w[nb][1].z, w[nb][1].w};
     uint32_t h[8], m[8], l[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) split3(ev[nb] ? v[i] : 0.0f, h[i], m[i], l[i]);
+    for (int i = 0; i < 8; ++i) split3(v[i], h[i], m[i], l[i]);
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     u32x4 ph, pm, pl;
 #pragma unroll
@@ -413,8 +413,7 @@ __device__ __forceinline__ void router_mma(f32x16 (&acc)[MBLK][NBLK], const bf16
 template <int R, int RD, int MBLK, int NBLK>
 __device__ __forceinline__ void router_round(f32x16 (&acc)[MBLK][NBLK],
                                              const bf16_t* const (&xp)[MBLK],
-                                             const float* const (&wp)[NBLK], const bool (&ev)[NBLK],
-                                             int rs) {
+                                             const float* const (&wp)[NBLK], int rs) {
   constexpr int D = RD < R ? RD : R;
   bf16x8 xa[R][MBLK];
 #pragma unroll
@@ -429,18 +428,60 @@ __device__ __forceinline__ void router_round(f32x16 (&acc)[MBLK][NBLK],
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < R; ++i) {
-    router_mma<MBLK, NBLK>(acc, xa[i], wr[i % D], ev);
+    router_mma<MBLK, NBLK>(acc, xa[i], wr[i % D]);
     if (i + D < R) load_w_slice<NBLK>(wr[i % D], wp, (rs + i + D) * 16);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Slices [s0, s0 + n), n a multiple of D and at least 2 D: one ring of D
+// slots, each holding a slice's x fragments and W_g values; the loads of
+// slice i + D go into the slot slice i frees.  Loads complete in issue
+// order as far as the wait counter is concerned, so x (from HBM) and W_g
+// (from L2) travel together D slices ahead: a shallower ring for either
+// would cap the lead of both.  Every load in the loop body is
+// unconditional, so every wait is an exact count.
+constexpr int kStreamDepth = 4;  // slices per ring of router_stream
+
+template <int D, int MBLK, int NBLK>
+__device__ __forceinline__ void router_stream(f32x16 (&acc)[MBLK][NBLK],
+                                              const bf16_t* const (&xp)[MBLK],
+                                              const float* const (&wp)[NBLK], int s0, int n) {
+  bf16x8 xa[D][MBLK];
+  float4 wr[D][NBLK][2];
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+#pragma unroll
+    for (int mb = 0; mb < MBLK; ++mb) xa[i][mb] = *reinterpret_cast<const bf16x8*>(xp[mb] + (s0 + i) * 16);
+    load_w_slice<NBLK>(wr[i], wp, (s0 + i) * 16);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  int s = s0;
+  for (; s + D < s0 + n; s += D) {  // every block of D slices but the last
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      router_mma<MBLK, NBLK>(acc, xa[i], wr[i]);
+#pragma unroll
+      for (int mb = 0; mb < MBLK; ++mb)
+        xa[i][mb] = *reinterpret_cast<const bf16x8*>(xp[mb] + (s + D + i) * 16);
+      load_w_slice<NBLK>(wr[i], wp, (s + D + i) * 16);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    router_mma<MBLK, NBLK>(acc, xa[i], wr[i]);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // One workgroup: 32*MBLK tokens x 32*NBLK experts, kRW wavefronts.  The
 // d/16 K slices are cut into kRW contiguous ranges, one per wavefront.  A
-// wavefront loads the x fragments of up to RS slices at once (one trip to
-// HBM per round) and streams W_g, which every workgroup reads and so stays
-// in L2, through a ring of RD slices in registers; each W_g value is split
-// once for all MBLK token blocks.  The partial logit tiles are summed in
+// range of whole ring blocks streams x and W_g (which every workgroup reads
+// and so stays in L2) through router_stream's ring; other ranges load the
+// x fragments of up to RS slices at once (one trip to HBM per round) and
+// stream W_g through a ring of RD slices.  Each W_g value is split once for
+// all MBLK token blocks.  The partial logit tiles are summed in
 // LDS in wavefront order (deterministic), then each wavefront selects for
 // four tokens at a time.
 //
@@ -480,14 +521,13 @@ __global__ __launch_bounds__(kRW * kWave) void router_mfma_kernel(
     xp[mb] = x + (t < T ? t : static_cast<int64_t>(T) - 1) * d + kh;
   }
   // Rows of the logit tile: the N_r experts of W_g, then, for noisy gating
-  // (wn set), the N_r rows of W_noise (2 N_r <= 32*NBLK).
+  // (wn set), the N_r rows of W_noise (2 N_r <= 32*NBLK).  Tile rows past
+  // them read the last real row again; their logit columns are never read.
   const int NE = wn != nullptr ? 2 * Nr : Nr;
   const float* wp[NBLK];
-  bool ev[NBLK];
 #pragma unroll
   for (int nb = 0; nb < NBLK; ++nb) {
     const int e = min(nb * 32 + lr, NE - 1);
-    ev[nb] = nb * 32 + lr < NE;
     wp[nb] = (e < Nr ? wg + static_cast<int64_t>(e) * d : wn + static_cast<int64_t>(e - Nr) * d) + kh;
   }
 
@@ -504,13 +544,19 @@ __global__ __launch_bounds__(kRW * kWave) void router_mfma_kernel(
   const int s0 = range * S / nranges, s1 = (range + 1) * S / nranges;
   // Full rounds of RS slices, then the remainder in rounds of 8, 4, 2, 1.
   int rs = s0;
-  for (; rs + RS <= s1; rs += RS) router_round<RS, RD, MBLK, NBLK>(acc, xp, wp, ev, rs);
-  if constexpr (RS > 8) {
-    if (rs + 8 <= s1) { router_round<8, RD, MBLK, NBLK>(acc, xp, wp, ev, rs); rs += 8; }
+  // Ranges that are whole blocks of kStreamDepth slices stream; the rest
+  // (and short ranges) go round by round.
+  if (s1 - s0 >= 2 * kStreamDepth && (s1 - s0) % kStreamDepth == 0) {
+    router_stream<kStreamDepth, MBLK, NBLK>(acc, xp, wp, s0, s1 - s0);
+    rs = s1;
   }
-  if (rs + 4 <= s1) { router_round<4, RD, MBLK, NBLK>(acc, xp, wp, ev, rs); rs += 4; }
-  if (rs + 2 <= s1) { router_round<2, RD, MBLK, NBLK>(acc, xp, wp, ev, rs); rs += 2; }
-  if (rs + 1 <= s1) router_round<1, RD, MBLK, NBLK>(acc, xp, wp, ev, rs);
+  for (; rs + RS <= s1; rs += RS) router_round<RS, RD, MBLK, NBLK>(acc, xp, wp, rs);
+  if constexpr (RS > 8) {
+    if (rs + 8 <= s1) { router_round<8, RD, MBLK, NBLK>(acc, xp, wp, rs); rs += 8; }
+  }
+  if (rs + 4 <= s1) { router_round<4, RD, MBLK, NBLK>(acc, xp, wp, rs); rs += 4; }
+  if (rs + 2 <= s1) { router_round<2, RD, MBLK, NBLK>(acc, xp, wp, rs); rs += 2; }
+  if (rs + 1 <= s1) router_round<1, RD, MBLK, NBLK>(acc, xp, wp, rs);
 
   // Sum of the wavefronts' partial tiles in wavefront order: each writes its
   // tile to its own LDS slot, then every thread adds its elements' kRW
