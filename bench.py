@@ -6,9 +6,10 @@
 A step is one moe_forward (router, dispatch, routed gate/up and down grouped
 GEMMs, shared experts, combine) over one batch of seeded synthetic inputs
 that are resident in HBM before timing starts.  By default the expert
-weights are converted once to the packed layout (moe_pack_weights) before
-timing, as a server would at load time; --weights row_major times the plain
-layout, and the JSON line carries the other layout's time beside it.  The timed steps run through
+weights and the router weights are converted once to their packed layouts
+(moe_pack_weights, moe_pack_router) before timing, as a server would at load
+time; --weights row_major times the plain layouts, and the JSON line carries
+the other layouts' time beside it.  The timed steps run through
 moe_forward_timed with a HIP event pair for the gate/up kernel only, bound
 to its launch on the launch stream (the kernel's own start and end); the
 per-stage breakdown comes from a few further steps with every marker set,
@@ -178,9 +179,14 @@ class Bench:
         self.layout = weights if self.packable else "row_major"
         self.rm_args = [d["x"], d["w_router"], d["bias"], *[d[k] for k in self.weight_keys]]
         if self.layout == "packed":
-            self.lay = dataclasses.replace(self.lay_rm, weight_layout="packed")
+            # The router's packed order needs the matrix-core router (bf16,
+            # d % 64, N_r <= 128).
+            rpk = cfg.d_model % 64 == 0 and cfg.n_routed <= 128
+            self.lay = dataclasses.replace(self.lay_rm, weight_layout="packed",
+                                           router_layout="packed" if rpk else "row_major")
             pk = {k: ops.pack_weights(self.lay_rm, d[k]) for k in self.weight_keys}
-            self.call_args = [d["x"], d["w_router"], d["bias"], *[pk[k] for k in self.weight_keys]]
+            w_router = ops.pack_router(self.lay_rm, d["w_router"]) if rpk else d["w_router"]
+            self.call_args = [d["x"], w_router, d["bias"], *[pk[k] for k in self.weight_keys]]
         else:
             self.lay = self.lay_rm
             self.call_args = self.rm_args
@@ -459,7 +465,8 @@ def decode_side(args, dev):
         "workload": f"DeepSeekMoE {cfg.name} layer forward: T={cfg.tokens}, d={cfg.d_model}, "
                     f"{cfg.n_routed} routed (top-{cfg.top_k}) + {cfg.n_shared} shared experts, "
                     f"SiLU FFN width {cfg.d_ff}, {cfg.gate}",
-        "tokens": cfg.tokens, "weights": b.layout, "steps": steps, "warmup_run": warm,
+        "tokens": cfg.tokens, "weights": b.layout, "router_weights": b.lay.router_layout,
+        "steps": steps, "warmup_run": warm,
         "ms_per_step": ms, "tokens_per_s": cfg.tokens / (ms * 1e-3),
         "layer_algorithmic_bytes": lb,
         "layer_hbm_gbs": lb / (ms * 1e-3) / 1e9,
@@ -527,7 +534,7 @@ def main():
                         f"SiLU FFN width {I}, {cfg.gate}",
             "tokens": T, "d_model": dm, "n_routed": cfg.n_routed, "n_shared": cfg.n_shared,
             "top_k": K, "d_ff": I, "gate": cfg.gate, "parallelism": "single GPU",
-            "weights": b.layout,
+            "weights": b.layout, "router_weights": b.lay.router_layout,
         },
         "weights": b.layout,
         "layer_algorithmic_bytes": layer_bytes,
@@ -563,17 +570,18 @@ def main():
         # Routing statistics next to the plain router on the same batch.
         d, p, lib, c_layer, stream = b.d, ops._p, b.lib, b.c_layer, b.stream
         n_dev = 8 if cfg.n_routed % 8 == 0 else 1
-        s_idx, s_w, s_stats, s_lse = ops.route_stats(b.lay, d["x"], d["w_router"], d["bias"], n_dev,
+        w_router = b.call_args[1]     # in the timed forward's router layout
+        s_idx, s_w, s_stats, s_lse = ops.route_stats(b.lay, d["x"], w_router, d["bias"], n_dev,
                                                      lse=True, ws=b.fwd.ws)
 
         def route_plain():
             _lib.check("moe_route", lib.moe_route(ctypes.byref(c_layer), T, p(d["x"]),
-                                                  p(d["w_router"]), p(d["bias"]), p(s_idx), p(s_w),
+                                                  p(w_router), p(d["bias"]), p(s_idx), p(s_w),
                                                   stream))
 
         def route_with_stats():
             _lib.check("moe_route_stats", lib.moe_route_stats(
-                ctypes.byref(c_layer), T, p(d["x"]), p(d["w_router"]), p(d["bias"]), n_dev,
+                ctypes.byref(c_layer), T, p(d["x"]), p(w_router), p(d["bias"]), n_dev,
                 p(s_idx), p(s_w), p(s_stats), p(s_lse), p(b.fwd.ws), b.fwd.ws.numel(), stream))
 
         out["routing_stats"] = {"route_ms": per_call_ms(route_plain),

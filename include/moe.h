@@ -25,7 +25,9 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Every call only enqueues work on it and returns.
  *   - Weights are [out_features, in_features] (in_features contiguous):
- *       w_router [N_r, d] fp32 (row i is the centroid e_i),
+ *       w_router [N_r, d] fp32 (row i is the centroid e_i; with
+ *         layer->router_layout == MOE_ROUTER_PACKED, the order written by
+ *         moe_pack_router instead),
  *       w_gate, w_up [N_r, I, d], w_down [N_r, d, I],
  *       ws_gate, ws_up [K_s, I_s, d], ws_down [K_s, d, I_s].
  *     x, y, expert weights and intermediate buffers use layer->dtype
@@ -54,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum {
   MOE_OK = 0,
@@ -107,6 +109,26 @@ typedef enum {
   MOE_WEIGHTS_PACKED = 1
 } moe_weight_layout;
 
+/* Storage order of the router weights w_router. */
+typedef enum {
+  /* [N_r, d] fp32 row-major.                                             */
+  MOE_ROUTER_ROW_MAJOR = 0,
+  /* The order written by moe_pack_router: the order in which the bf16
+     matrix-core router reads W_g, so that every load instruction of it
+     reads 1 KB of contiguous memory.  The N_r rows are padded to
+     R = MOE_ROUTER_PAD_ROWS(N_r) rows (rows N_r .. R-1 repeat row N_r - 1)
+     and element (e, k) of the padded [R, d] matrix sits at float index
+       ((k/16 * R/32 + e/32) * 2 + (k%8)/4) * 256 + (e%32 + 32*((k%16)/8)) * 4
+       + k%4.
+     Requires dtype MOE_BF16, d % 64 == 0 and N_r <= 128; moe_route_noisy
+     does not take it (MOE_ERR_UNSUPPORTED).  No arithmetic changes: the
+     router's results are bit-identical to the row-major order.            */
+  MOE_ROUTER_PACKED = 1
+} moe_router_layout;
+
+/* Rows of the packed router matrix for N_r routed experts (N_r <= 128). */
+#define MOE_ROUTER_PAD_ROWS(n_routed) ((n_routed) <= 32 ? 32 : (n_routed) <= 64 ? 64 : 128)
+
 typedef enum {
   /* g_i = s_i on the top-K' of s = Softmax over N_r routed experts, not
      renormalised (DeepSeekMoE page, section 3.2, eq. 10-11).            */
@@ -142,6 +164,7 @@ typedef struct {
   int32_t ffn;          /* moe_ffn                                     */
   int32_t bias_mode;    /* moe_bias_mode                               */
   int32_t weight_layout;/* moe_weight_layout                           */
+  int32_t router_layout;/* moe_router_layout                           */
 } moe_layer;
 
 int moe_abi_version(void);
@@ -167,7 +190,9 @@ int moe_route(const moe_layer* layer, int64_t T, const void* x, const float* w_r
  * takes the place of the logits for both the selection and the gate values
  * (logit_bias is added to H as layer->bias_mode says).  The method's random
  * numbers are an input: noise [T, N_r] fp32 holds the caller's standard
- * normal draws; w_noise [N_r, d] fp32.  Softplus(v) = log(1 + e^v).  The
+ * normal draws; w_noise [N_r, d] fp32.  Softplus(v) = log(1 + e^v).
+ * w_router must be row-major (layer->router_layout MOE_ROUTER_ROW_MAJOR,
+ * else MOE_ERR_UNSUPPORTED).  The
  * rest of the layer is the staged path: moe_permute, moe_expert_ffn,
  * moe_shared_ffn, moe_combine. */
 int moe_route_noisy(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
@@ -183,6 +208,13 @@ int moe_route_noisy(const moe_layer* layer, int64_t T, const void* x, const floa
  * fields are checked as everywhere but not used. */
 int moe_pack_weights(const moe_layer* layer, int64_t count, int32_t rows, int32_t cols,
                      const void* src, void* dst, void* stream);
+
+/* Router weight packing (once, before inference; no compute of the layer):
+ * dst [MOE_ROUTER_PAD_ROWS(N_r) * d] fp32 = w_router [N_r, d] fp32 in the
+ * MOE_ROUTER_PACKED order.  dst must not overlap w_router.  The layer must
+ * meet that layout's requirements (dtype MOE_BF16, d % 64 == 0, N_r <= 128;
+ * else MOE_ERR_UNSUPPORTED) whatever its router_layout field says. */
+int moe_pack_router(const moe_layer* layer, const float* w_router, float* dst, void* stream);
 
 /* Floats written to `stats` by moe_route_stats for N_r experts, D groups. */
 #define MOE_STATS_LEN(n_routed, n_devices) (2 * (n_routed) + 2 * (n_devices) + 3)

@@ -17,10 +17,16 @@ MOE_GATE_SOFTMAX_TOPK, MOE_GATE_TOPK_SOFTMAX = 0, 1
 MOE_FFN_SILU_GATED, MOE_FFN_RELU = 0, 1
 MOE_BIAS_LOGITS, MOE_BIAS_SELECTION = 0, 1
 MOE_WEIGHTS_ROW_MAJOR, MOE_WEIGHTS_PACKED = 0, 1
+MOE_ROUTER_ROW_MAJOR, MOE_ROUTER_PACKED = 0, 1
+
+
+def router_pad_rows(n_routed: int) -> int:
+    """MOE_ROUTER_PAD_ROWS: rows of the packed router matrix."""
+    return 32 if n_routed <= 32 else 64 if n_routed <= 64 else 128
 
 EXPORTS = (
     "moe_abi_version", "moe_status_str", "moe_last_hip_error", "moe_workspace_size",
-    "moe_pack_weights", "moe_route", "moe_route_noisy", "moe_route_stats", "moe_permute", "moe_expert_ffn", "moe_shared_ffn", "moe_combine",
+    "moe_pack_weights", "moe_pack_router", "moe_route", "moe_route_noisy", "moe_route_stats", "moe_permute", "moe_expert_ffn", "moe_shared_ffn", "moe_combine",
     "moe_forward", "moe_forward_timed", "moe_forward_noalloc",
 )
 MOE_NUM_STAGES = 7
@@ -31,7 +37,7 @@ STAGES = ("route", "dispatch", "routed_gate_up", "routed_down", "shared_gate_up"
 class MoeLayer(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "d_model", "n_routed", "n_shared", "top_k", "d_ff", "d_ff_shared", "gate", "dtype",
-        "capacity", "group_size", "ffn", "bias_mode", "weight_layout")]
+        "capacity", "group_size", "ffn", "bias_mode", "weight_layout", "router_layout")]
 
 
 class MoeError(RuntimeError):
@@ -57,6 +63,7 @@ _SIGS = {
     "moe_workspace_size": ([LP, I64, ctypes.POINTER(SZ)], ctypes.c_int),
     "moe_route": ([LP, I64, P, P, P, P, P, P], ctypes.c_int),
     "moe_pack_weights": ([LP, I64, ctypes.c_int32, ctypes.c_int32, P, P, P], ctypes.c_int),
+    "moe_pack_router": ([LP, P, P, P], ctypes.c_int),
     "moe_route_noisy": ([LP, I64, P, P, P, P, P, P, P, P], ctypes.c_int),
     "moe_route_stats": ([LP, I64, P, P, P, ctypes.c_int32, P, P, P, P, P, SZ, P], ctypes.c_int),
     "moe_permute": ([LP, I64, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),

@@ -90,6 +90,11 @@ Layout layout_of(const moe_layer* L, int64_t T) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The packed router order is read only by the bf16 matrix-core router.
+bool router_packable(const moe_layer* L) {
+  return L->dtype == MOE_BF16 && L->d_model % 64 == 0 && L->n_routed <= 128;
+}
+
 int check_layer(const moe_layer* L, int64_t T) {
   if (L == nullptr || T < 0) return MOE_ERR_INVALID_ARG;
   if (L->dtype != MOE_F32 && L->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
@@ -101,6 +106,8 @@ int check_layer(const moe_layer* L, int64_t T) {
   if (L->ffn != MOE_FFN_SILU_GATED && L->ffn != MOE_FFN_RELU) return MOE_ERR_INVALID_ARG;
   if (L->bias_mode != MOE_BIAS_LOGITS && L->bias_mode != MOE_BIAS_SELECTION) return MOE_ERR_INVALID_ARG;
   if (L->weight_layout != MOE_WEIGHTS_ROW_MAJOR && L->weight_layout != MOE_WEIGHTS_PACKED)
+    return MOE_ERR_INVALID_ARG;
+  if (L->router_layout != MOE_ROUTER_ROW_MAJOR && L->router_layout != MOE_ROUTER_PACKED)
     return MOE_ERR_INVALID_ARG;
   if (L->top_k < 1 || L->top_k > L->n_routed || L->top_k > 16) return MOE_ERR_INVALID_ARG;
   if (L->n_routed > 256) return MOE_ERR_UNSUPPORTED;
@@ -129,6 +136,7 @@ int check_layer(const moe_layer* L, int64_t T) {
     if (L->dtype != MOE_BF16 || L->d_model % r != 0 || L->d_ff % r != 0) return MOE_ERR_UNSUPPORTED;
     if (L->n_shared > 0 && L->d_ff_shared % r != 0) return MOE_ERR_UNSUPPORTED;
   }
+  if (L->router_layout == MOE_ROUTER_PACKED && !router_packable(L)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -382,6 +390,7 @@ static moe::RouteArgs route_args(const moe_layer* layer, int64_t T, const void* 
   a.gate = layer->gate;
   a.bias_sel = layer->bias_mode == MOE_BIAS_SELECTION;
   a.x_bf16 = layer->dtype == MOE_BF16;
+  a.w_packed = layer->router_layout == MOE_ROUTER_PACKED;
   a.topk_idx = topk_idx;
   a.topk_w = topk_w;
   return a;
@@ -407,10 +416,25 @@ int moe_pack_weights(const moe_layer* layer, int64_t count, int32_t rows, int32_
   return MOE_OK;
 }
 
+int moe_pack_router(const moe_layer* layer, const float* w_router, float* dst, void* stream) {
+  MOE_TRY(check_layer(layer, 0));
+  if (!router_packable(layer)) return MOE_ERR_UNSUPPORTED;
+  MOE_TRY(need(w_router));
+  MOE_TRY(need(dst));
+  const int64_t nsrc = static_cast<int64_t>(layer->n_routed) * layer->d_model * 4;
+  const int64_t ndst = static_cast<int64_t>(moe::router_pad_rows(layer->n_routed)) * layer->d_model * 4;
+  const auto s0 = reinterpret_cast<uintptr_t>(w_router), d0 = reinterpret_cast<uintptr_t>(dst);
+  if (s0 < d0 + ndst && d0 < s0 + nsrc) return MOE_ERR_INVALID_ARG;
+  MOE_HIP(moe::launch_pack_router(w_router, dst, layer->d_model, layer->n_routed,
+                                  static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
 int moe_route_noisy(const moe_layer* layer, int64_t T, const void* x, const float* w_router,
                     const float* logit_bias, const float* w_noise, const float* noise,
                     int32_t* topk_idx, float* topk_w, void* stream) {
   MOE_TRY(check_layer(layer, T));
+  if (layer->router_layout != MOE_ROUTER_ROW_MAJOR) return MOE_ERR_UNSUPPORTED;
   MOE_TRY(needT(x, T));
   MOE_TRY(need(w_router));
   MOE_TRY(opt(logit_bias));

@@ -21,6 +21,7 @@ struct RouteArgs {
   float* lse;              // [T] or null: per-token log-sum-exp (statistics only)
   const float* w_noise;    // [N_r, d] or null: noisy top-k gating (no split, no statistics)
   const float* noise;      // [T, N_r] standard normal draws, with w_noise
+  bool w_packed;           // w_router in the packed order of launch_pack_router
 };
 // Split-K of the matrix-core router for small batches: at most this many
 // K slices, each writing a [T, 128] fp32 partial tile.
@@ -29,6 +30,12 @@ inline size_t router_partial_bytes(int64_t T) {
   return T < 4096 ? static_cast<size_t>(kRouterSplit) * static_cast<size_t>(T) * 128 * 4 : 0;
 }
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+
+// Rows of the matrix-core router's logit tile for N_r <= 128 experts (the
+// packed W_g holds this many rows of d floats).
+inline int router_pad_rows(int Nr) { return Nr <= 32 ? 32 : Nr <= 64 ? 64 : 128; }
+// W_g [N_r, d] -> its packed order (moe_pack_router), d % 16 == 0.
+hipError_t launch_pack_router(const float* wg, float* dst, int d, int Nr, hipStream_t s);
 
 // Routing statistics: every router workgroup (at least 32 tokens each) sums
 // its tokens' softmax values, choices and squared log-sum-exps into one row

@@ -360,15 +360,28 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t first, uint32_t second) {
 
 constexpr int kRW = 8;   // wavefronts per matrix-core router workgroup
 
-// W_g values for one 16-wide K slice: lane l holds 8 consecutive k of
-// expert row nb*32 + l%32.
-template <int NBLK>
+// W_g values for K slice s (k = 16s .. 16s+15): lane l holds the 8
+// consecutive k of expert row nb*32 + l%32 starting at 16s + 8*(l/32), as
+// two float4.  Row-major W_g: wp[nb] points at that row (plus the lane's k
+// half), and a load instruction touches 32 rows, 32 bytes of each.  Packed
+// W_g (moe_pack_router): the float4 of (s, nb, half j, lane l) is number
+// ((s*NBLK + nb)*2 + j)*64 + l, so each load instruction reads 1 KB of
+// contiguous memory; wp[nb] points at (nb, lane) of slice 0.
+constexpr int kPackSliceFloats = 512;   // packed floats per (slice, 32-row block)
+
+template <int NBLK, bool PK>
 __device__ __forceinline__ void load_w_slice(float4 (&w)[NBLK][2], const float* const (&wp)[NBLK],
-                                             int off) {
+                                             int s) {
 #pragma unroll
   for (int nb = 0; nb < NBLK; ++nb) {
-    w[nb][0] = *reinterpret_cast<const float4*>(wp[nb] + off);
-    w[nb][1] = *reinterpret_cast<const float4*>(wp[nb] + off + 4);
+    if constexpr (PK) {
+      const float* q = wp[nb] + s * NBLK * kPackSliceFloats;
+      w[nb][0] = *reinterpret_cast<const float4*>(q);
+      w[nb][1] = *reinterpret_cast<const float4*>(q + kPackSliceFloats / 2);
+    } else {
+      w[nb][0] = *reinterpret_cast<const float4*>(wp[nb] + s * 16);
+      w[nb][1] = *reinterpret_cast<const float4*>(wp[nb] + s * 16 + 4);
+    }
   }
 }
 
@@ -410,7 +423,7 @@ __device__ __forceinline__ void router_mma(f32x16 (&acc)[MBLK][NBLK], const bf16
 // R consecutive K slices starting at slice rs: every x fragment is loaded
 // up front (one trip to HBM), W_g streams through a ring of min(RD, R)
 // slices.  No branches, so every wait on a load is an exact count.
-template <int R, int RD, int MBLK, int NBLK>
+template <int R, int RD, int MBLK, int NBLK, bool PK>
 __device__ __forceinline__ void router_round(f32x16 (&acc)[MBLK][NBLK],
                                              const bf16_t* const (&xp)[MBLK],
                                              const float* const (&wp)[NBLK], int rs) {
@@ -422,73 +435,125 @@ __device__ __forceinline__ void router_round(f32x16 (&acc)[MBLK][NBLK],
     for (int mb = 0; mb < MBLK; ++mb) xa[i][mb] = *reinterpret_cast<const bf16x8*>(xp[mb] + (rs + i) * 16);
   float4 wr[D][NBLK][2];
 #pragma unroll
-  for (int i = 0; i < D; ++i) load_w_slice<NBLK>(wr[i], wp, (rs + i) * 16);
+  for (int i = 0; i < D; ++i) load_w_slice<NBLK, PK>(wr[i], wp, rs + i);
   // Keep every load above at the top: the scheduler would otherwise sink
   // them next to their first use and serialise the round trips.
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     router_mma<MBLK, NBLK>(acc, xa[i], wr[i % D]);
-    if (i + D < R) load_w_slice<NBLK>(wr[i % D], wp, (rs + i + D) * 16);
+    if (i + D < R) load_w_slice<NBLK, PK>(wr[i % D], wp, rs + i + D);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Slices [s0, s0 + n), n a multiple of D and at least 2 D: one ring of D
-// slots, each holding a slice's x fragments and W_g values; the loads of
-// slice i + D go into the slot slice i frees.  Loads complete in issue
-// order as far as the wait counter is concerned, so x (from HBM) and W_g
-// (from L2) travel together D slices ahead: a shallower ring for either
-// would cap the lead of both.  Every load in the loop body is
-// unconditional, so every wait is an exact count.
-constexpr int kStreamDepth = 4;  // slices per ring of router_stream
+// Streamed K ranges: blocks of four slices (64 k, one 128-byte line of
+// every token row).  A block's x rows go global -> LDS by DMA
+// (buffer_load ... lds, 16 bytes per lane, eight lanes per 128-byte row
+// segment, so each load instruction moves 8 whole lines) into a two-block
+// ring private to the wavefront; the MFMA fragments are then read from LDS.
+// Loaded straight into registers, a fragment load touches 32 token rows,
+// 32 bytes of each, and every line of x is requested four times.  Chunk c
+// of ring row r sits at position c ^ xswz(r), which keeps the 16-byte
+// fragment reads of 16 consecutive rows on distinct banks.
+__device__ __forceinline__ int xswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-template <int D, int MBLK, int NBLK>
-__device__ __forceinline__ void router_stream(f32x16 (&acc)[MBLK][NBLK],
-                                              const bf16_t* const (&xp)[MBLK],
-                                              const float* const (&wp)[NBLK], int s0, int n) {
-  bf16x8 xa[D][MBLK];
-  float4 wr[D][NBLK][2];
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// s_waitcnt with vmcnt <= N (gfx9 encoding: vmcnt in bits 3:0 and 15:14;
+// expcnt and lgkmcnt at their maxima, i.e. not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// The four slices of one ring block.  In flight on entry, in issue order:
+// the block's x DMA, its four slices of W_g, and (MORE) the next block's x
+// DMA.  After slice i the W_g loads of slice i of the next block are issued
+// into the registers slice i frees, so before slice i exactly 3*NW + ND
+// later loads may still be in flight (MORE), or (3 - i)*NW in the last
+// block.  Loads retire in issue order for the counter, so the wait for
+// slice i's W_g also covers this block's x DMA, issued before it.
+template <int MBLK, int NBLK, bool PK, bool MORE>
+__device__ __forceinline__ void stream_block(f32x16 (&acc)[MBLK][NBLK], float4 (&wr)[4][NBLK][2],
+                                             const float* const (&wp)[NBLK], int snext,
+                                             const bf16_t* cur, int lane) {
+  constexpr int ND = MBLK * 4;   // x DMA loads per block (8 rows each)
+  constexpr int NW = NBLK * 2;   // W_g loads per slice
+  const int r = lane & 31, h = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < D; ++i) {
-#pragma unroll
-    for (int mb = 0; mb < MBLK; ++mb) xa[i][mb] = *reinterpret_cast<const bf16x8*>(xp[mb] + (s0 + i) * 16);
-    load_w_slice<NBLK>(wr[i], wp, (s0 + i) * 16);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  int s = s0;
-  for (; s + D < s0 + n; s += D) {  // every block of D slices but the last
-#pragma unroll
-    for (int i = 0; i < D; ++i) {
-      router_mma<MBLK, NBLK>(acc, xa[i], wr[i]);
-#pragma unroll
-      for (int mb = 0; mb < MBLK; ++mb)
-        xa[i][mb] = *reinterpret_cast<const bf16x8*>(xp[mb] + (s + D + i) * 16);
-      load_w_slice<NBLK>(wr[i], wp, (s + D + i) * 16);
-      __builtin_amdgcn_sched_barrier(0);
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (MORE) {
+      wait_vmcnt<3 * NW + ND>();
+    } else {
+      if (i == 0) wait_vmcnt<3 * NW>();
+      else if (i == 1) wait_vmcnt<2 * NW>();
+      else if (i == 2) wait_vmcnt<NW>();
+      else wait_vmcnt<0>();
     }
-  }
+    // The DMA's LDS writes are not visible to the compiler: keep the
+    // fragment reads below the wait.
+    asm volatile("" ::: "memory");
+    bf16x8 xa[MBLK];
 #pragma unroll
-  for (int i = 0; i < D; ++i) {
-    router_mma<MBLK, NBLK>(acc, xa[i], wr[i]);
+    for (int mb = 0; mb < MBLK; ++mb) {
+      const int row = mb * 32 + r;
+      xa[mb] = *reinterpret_cast<const bf16x8*>(cur + row * 64 + ((2 * i + h) ^ xswz(row)) * 8);
+    }
+    router_mma<MBLK, NBLK>(acc, xa, wr[i]);
+    if constexpr (MORE) load_w_slice<NBLK, PK>(wr[i], wp, snext + i);
     __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+// Slices [s0, s0 + n), n a multiple of 4 and at least 8.  ring: this
+// wavefront's 2 * 32*MBLK * 64 bf16 of LDS; xoff: per-lane byte offsets of
+// its DMA chunks at k = 0 (the block's k goes in the scalar offset).
+template <int MBLK, int NBLK, bool PK>
+__device__ __forceinline__ void router_stream(f32x16 (&acc)[MBLK][NBLK], __amdgpu_buffer_rsrc_t rx,
+                                              const uint32_t (&xoff)[4 * MBLK],
+                                              const float* const (&wp)[NBLK], int s0, int n,
+                                              bf16_t* ring, int lane) {
+  constexpr int ND = MBLK * 4;
+  constexpr int BLK = 32 * MBLK * 64;   // bf16 per ring block
+  auto dma = [&](int b) {
+    const uint32_t so = static_cast<uint32_t>((s0 + 4 * b) * 16) * 2u;
+    bf16_t* dst = ring + (b & 1) * BLK;
+#pragma unroll
+    for (int q = 0; q < ND; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_ptr)(dst + q * 512), 16, xoff[q], so, 0, 0);
+  };
+  float4 wr[4][NBLK][2];
+  dma(0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) load_w_slice<NBLK, PK>(wr[i], wp, s0 + i);
+  __builtin_amdgcn_sched_barrier(0);
+  const int nblocks = n / 4;
+  int b = 0;
+  for (; b + 1 < nblocks; ++b) {
+    dma(b + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    stream_block<MBLK, NBLK, PK, true>(acc, wr, wp, s0 + 4 * (b + 1), ring + (b & 1) * BLK, lane);
+  }
+  stream_block<MBLK, NBLK, PK, false>(acc, wr, wp, 0, ring + (b & 1) * BLK, lane);
 }
 
 // One workgroup: 32*MBLK tokens x 32*NBLK experts, kRW wavefronts.  The
 // d/16 K slices are cut into kRW contiguous ranges, one per wavefront.  A
-// range of whole ring blocks streams x and W_g (which every workgroup reads
-// and so stays in L2) through router_stream's ring; other ranges load the
-// x fragments of up to RS slices at once (one trip to HBM per round) and
+// range of at least two whole blocks of four slices streams (router_stream:
+// x through an LDS ring, W_g - which every workgroup reads, so it stays in
+// L2 - into registers four slices ahead); other ranges load the x
+// fragments of up to RS slices at once (one trip to HBM per round) and
 // stream W_g through a ring of RD slices.  Each W_g value is split once for
 // all MBLK token blocks.  The partial logit tiles are summed in
 // LDS in wavefront order (deterministic), then each wavefront selects for
-// four tokens at a time.
+// four tokens at a time.  PK: W_g in the packed order of moe_pack_router.
 //
 // Small batches split K over KS workgroups per token block as well
 // (blockIdx.y); each then writes its summed tile to partial[ks][t][e] and
 // router_select_kernel finishes the sum in ks order and selects.
-template <int MBLK, int NBLK, bool STATS>
+template <int MBLK, int NBLK, bool STATS, bool PK>
 __global__ __launch_bounds__(kRW * kWave) void router_mfma_kernel(
     const bf16_t* __restrict__ x, const float* __restrict__ wg, const float* __restrict__ bias,
     int T, int d, int Nr, int K, int gate, bool bias_sel, int32_t* __restrict__ topk_idx,
@@ -521,14 +586,19 @@ __global__ __launch_bounds__(kRW * kWave) void router_mfma_kernel(
     xp[mb] = x + (t < T ? t : static_cast<int64_t>(T) - 1) * d + kh;
   }
   // Rows of the logit tile: the N_r experts of W_g, then, for noisy gating
-  // (wn set), the N_r rows of W_noise (2 N_r <= 32*NBLK).  Tile rows past
-  // them read the last real row again; their logit columns are never read.
+  // (wn set; row-major W_g only), the N_r rows of W_noise (2 N_r <=
+  // 32*NBLK).  Tile rows past them read the last real row again (the packed
+  // order repeats it); their logit columns are never read.
   const int NE = wn != nullptr ? 2 * Nr : Nr;
   const float* wp[NBLK];
 #pragma unroll
   for (int nb = 0; nb < NBLK; ++nb) {
-    const int e = min(nb * 32 + lr, NE - 1);
-    wp[nb] = (e < Nr ? wg + static_cast<int64_t>(e) * d : wn + static_cast<int64_t>(e - Nr) * d) + kh;
+    if constexpr (PK) {
+      wp[nb] = wg + nb * kPackSliceFloats + lane * 4;
+    } else {
+      const int e = min(nb * 32 + lr, NE - 1);
+      wp[nb] = (e < Nr ? wg + static_cast<int64_t>(e) * d : wn + static_cast<int64_t>(e - Nr) * d) + kh;
+    }
   }
 
   f32x16 acc[MBLK][NBLK];
@@ -539,30 +609,51 @@ __global__ __launch_bounds__(kRW * kWave) void router_mfma_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.0f;
 
+  // One LDS slot per wavefront: its x ring while it streams, then its
+  // partial logit tile (the ring is idle by then and private to the
+  // wavefront, so no barrier separates the two uses).
+  constexpr int SLOTF = TB * (NPAD > 64 ? NPAD : 64);
+  static_assert(SLOTF >= TB * NPAD && SLOTF * 4 >= 2 * TB * 128, "LDS slot");
+  __shared__ __align__(16) float slot[kRW][SLOTF];
+
   const int S = d / 16;
   const int range = blockIdx.y * kRW + wave, nranges = KS * kRW;
   const int s0 = range * S / nranges, s1 = (range + 1) * S / nranges;
   // Full rounds of RS slices, then the remainder in rounds of 8, 4, 2, 1.
   int rs = s0;
-  // Ranges that are whole blocks of kStreamDepth slices stream; the rest
-  // (and short ranges) go round by round.
-  if (s1 - s0 >= 2 * kStreamDepth && (s1 - s0) % kStreamDepth == 0) {
-    router_stream<kStreamDepth, MBLK, NBLK>(acc, xp, wp, s0, s1 - s0);
+  // Ranges of two or more whole blocks of four slices stream; the rest (and
+  // short ranges) go round by round.
+#if defined(__HIP_DEVICE_COMPILE__)  // buffer resources exist only in the device pass
+  if (s1 - s0 >= 8 && (s1 - s0) % 4 == 0) {
+    // x is below 4 GB (a layer requirement), so byte offsets fit 32 bits.
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16_t*>(x), 0, static_cast<uint32_t>(static_cast<int64_t>(T) * d * 2), 0x00020000);
+    // DMA chunk q of a block: ring row 8q + lane/8, position lane%8, which
+    // holds logical chunk (lane%8) ^ xswz(row) of that token's 64 k.
+    uint32_t xoff[4 * MBLK];
+#pragma unroll
+    for (int q = 0; q < 4 * MBLK; ++q) {
+      const int row = q * 8 + lane / 8;
+      const int64_t t = min(tok0 + row, static_cast<int64_t>(T) - 1);
+      xoff[q] = static_cast<uint32_t>(t * d * 2 + ((lane % 8) ^ xswz(row)) * 16);
+    }
+    router_stream<MBLK, NBLK, PK>(acc, rx, xoff, wp, s0, s1 - s0,
+                                  reinterpret_cast<bf16_t*>(&slot[wave][0]), lane);
     rs = s1;
   }
-  for (; rs + RS <= s1; rs += RS) router_round<RS, RD, MBLK, NBLK>(acc, xp, wp, rs);
+#endif
+  for (; rs + RS <= s1; rs += RS) router_round<RS, RD, MBLK, NBLK, PK>(acc, xp, wp, rs);
   if constexpr (RS > 8) {
-    if (rs + 8 <= s1) { router_round<8, RD, MBLK, NBLK>(acc, xp, wp, rs); rs += 8; }
+    if (rs + 8 <= s1) { router_round<8, RD, MBLK, NBLK, PK>(acc, xp, wp, rs); rs += 8; }
   }
-  if (rs + 4 <= s1) { router_round<4, RD, MBLK, NBLK>(acc, xp, wp, rs); rs += 4; }
-  if (rs + 2 <= s1) { router_round<2, RD, MBLK, NBLK>(acc, xp, wp, rs); rs += 2; }
-  if (rs + 1 <= s1) router_round<1, RD, MBLK, NBLK>(acc, xp, wp, rs);
+  if (rs + 4 <= s1) { router_round<4, RD, MBLK, NBLK, PK>(acc, xp, wp, rs); rs += 4; }
+  if (rs + 2 <= s1) { router_round<2, RD, MBLK, NBLK, PK>(acc, xp, wp, rs); rs += 2; }
+  if (rs + 1 <= s1) router_round<1, RD, MBLK, NBLK, PK>(acc, xp, wp, rs);
 
   // Sum of the wavefronts' partial tiles in wavefront order: each writes its
   // tile to its own LDS slot, then every thread adds its elements' kRW
   // values in order (the same additions as accumulating wave by wave).
   // D[row][col] of a 32x32 block: lane (col + 32*h), register v, row 8*(v/4) + 4*h + v%4.
-  __shared__ __align__(16) float slot[kRW][TB * NPAD];
 #pragma unroll
   for (int mb = 0; mb < MBLK; ++mb)
 #pragma unroll
@@ -673,20 +764,20 @@ __global__ __launch_bounds__(kWave) void router_select_kernel(
   select_and_store<NP, EPL>(z, zg, bias_sel, e, evq, t, K, gate, grp, lane, topk_idx, topk_w);
 }
 
-template <int MBLK, int NBLK>
-hipError_t launch_mfma(const RouteArgs& a, hipStream_t s, int* nblk) {
+template <int MBLK, int NBLK, bool PK>
+hipError_t launch_mfma_w(const RouteArgs& a, hipStream_t s, int* nblk) {
   constexpr int TB = 32 * MBLK;
   const int blocks = (a.T + TB - 1) / TB;
   *nblk = blocks;
   if (a.stats_part != nullptr) {
-    hipLaunchKernelGGL((router_mfma_kernel<MBLK, NBLK, true>), dim3(blocks, 1), dim3(kRW * kWave), 0,
+    hipLaunchKernelGGL((router_mfma_kernel<MBLK, NBLK, true, PK>), dim3(blocks, 1), dim3(kRW * kWave), 0,
                        s, static_cast<const bf16_t*>(a.x), a.w_router, a.bias, a.T, a.d,
                        a.n_routed, a.top_k, a.gate, a.bias_sel, a.topk_idx, a.topk_w, 1, nullptr,
                        a.stats_part, a.lse, nullptr, nullptr);
     return hipGetLastError();
   }
   if (a.w_noise != nullptr) {
-    hipLaunchKernelGGL((router_mfma_kernel<MBLK, NBLK, false>), dim3(blocks, 1), dim3(kRW * kWave), 0,
+    hipLaunchKernelGGL((router_mfma_kernel<MBLK, NBLK, false, PK>), dim3(blocks, 1), dim3(kRW * kWave), 0,
                        s, static_cast<const bf16_t*>(a.x), a.w_router, a.bias, a.T, a.d,
                        a.n_routed, a.top_k, a.gate, a.bias_sel, a.topk_idx, a.topk_w, 1, nullptr,
                        nullptr, nullptr, a.w_noise, a.noise);
@@ -694,7 +785,7 @@ hipError_t launch_mfma(const RouteArgs& a, hipStream_t s, int* nblk) {
   }
   // Split K when the token blocks alone would leave most CUs idle.
   const int KS = (a.partial != nullptr && MBLK == 1) ? max(1, min(kRouterSplit, 128 / blocks)) : 1;
-  hipLaunchKernelGGL((router_mfma_kernel<MBLK, NBLK, false>), dim3(blocks, KS), dim3(kRW * kWave), 0, s,
+  hipLaunchKernelGGL((router_mfma_kernel<MBLK, NBLK, false, PK>), dim3(blocks, KS), dim3(kRW * kWave), 0, s,
                      static_cast<const bf16_t*>(a.x), a.w_router, a.bias, a.T, a.d, a.n_routed,
                      a.top_k, a.gate, a.bias_sel, a.topk_idx, a.topk_w, KS, a.partial, nullptr,
                      nullptr, nullptr, nullptr);
@@ -705,6 +796,12 @@ hipError_t launch_mfma(const RouteArgs& a, hipStream_t s, int* nblk) {
                      a.partial, a.bias, a.T, a.n_routed, a.top_k, a.gate, a.bias_sel, KS, a.topk_idx,
                      a.topk_w);
   return hipGetLastError();
+}
+
+template <int MBLK, int NBLK>
+hipError_t launch_mfma(const RouteArgs& a, hipStream_t s, int* nblk) {
+  return a.w_packed ? launch_mfma_w<MBLK, NBLK, true>(a, s, nblk)
+                    : launch_mfma_w<MBLK, NBLK, false>(a, s, nblk);
 }
 
 template <typename XT>
@@ -719,6 +816,8 @@ hipError_t launch_x(const RouteArgs& a, hipStream_t s, int* nblk) {
 }
 
 hipError_t launch_router(const RouteArgs& a, hipStream_t s, int* nblk) {
+  // Packed W_g is only read by the matrix-core kernel; the host accepts it
+  // only where that kernel runs (bf16 x, d % 64 == 0, N_r <= 128, no noise).
   if (a.x_bf16 && a.d % 64 == 0) {
     // Two token blocks per wavefront once there are enough tokens to fill
     // the chip with 64-token workgroups.  Noisy gating needs 2 N_r rows.
@@ -822,7 +921,33 @@ __global__ __launch_bounds__(kFoldThreads) void route_stats_kernel(
   }
 }
 
+// moe_pack_router: W_g [N_r, d] row-major -> the packed order (see
+// load_w_slice), one float4 per thread.  Rows past N_r up to router_pad_rows
+// repeat row N_r - 1, as the row-major kernel reads them.
+__global__ __launch_bounds__(256) void pack_router_kernel(const float* __restrict__ wg,
+                                                          float* __restrict__ dst, int d, int Nr,
+                                                          int nblk) {
+  const int64_t n4 = static_cast<int64_t>(d / 16) * nblk * 128;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= n4) return;
+  const int l = static_cast<int>(idx & 63);
+  const int j = static_cast<int>((idx >> 6) & 1);
+  const int nb = static_cast<int>((idx >> 7) % nblk);
+  const int64_t sl = idx / (static_cast<int64_t>(nblk) * 128);
+  const int e = min(nb * 32 + (l & 31), Nr - 1);
+  const int64_t k = 16 * sl + 8 * (l >> 5) + 4 * j;
+  reinterpret_cast<float4*>(dst)[idx] = *reinterpret_cast<const float4*>(wg + static_cast<int64_t>(e) * d + k);
+}
+
 }  // namespace
+
+hipError_t launch_pack_router(const float* wg, float* dst, int d, int Nr, hipStream_t s) {
+  const int nblk = router_pad_rows(Nr) / 32;
+  const int64_t n4 = static_cast<int64_t>(d / 16) * nblk * 128;
+  hipLaunchKernelGGL(pack_router_kernel, dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256), 0, s,
+                     wg, dst, d, Nr, nblk);
+  return hipGetLastError();
+}
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;

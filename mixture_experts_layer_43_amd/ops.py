@@ -21,6 +21,7 @@ _GATE = {"softmax_topk": _lib.MOE_GATE_SOFTMAX_TOPK, "topk_softmax": _lib.MOE_GA
 _FFN = {"silu": _lib.MOE_FFN_SILU_GATED, "relu": _lib.MOE_FFN_RELU}
 _BIAS = {"logits": _lib.MOE_BIAS_LOGITS, "selection": _lib.MOE_BIAS_SELECTION}
 _LAYOUT = {"row_major": _lib.MOE_WEIGHTS_ROW_MAJOR, "packed": _lib.MOE_WEIGHTS_PACKED}
+_RLAYOUT = {"row_major": _lib.MOE_ROUTER_ROW_MAJOR, "packed": _lib.MOE_ROUTER_PACKED}
 
 
 @dataclass(frozen=True)
@@ -40,13 +41,15 @@ class Layer:
     ffn: str = "silu"       # "silu" (W1, W3, W2) or "relu" (wi = w_gate, wo = w_down)
     bias_mode: str = "logits"  # "logits": bias in selection and gates; "selection": selection only
     weight_layout: str = "row_major"  # or "packed" (weights converted by pack_weights)
+    router_layout: str = "row_major"  # or "packed" (w_router converted by pack_router)
 
     @classmethod
     def of(cls, cfg) -> "Layer":
         return cls(cfg.d_model, cfg.n_routed, cfg.n_shared, cfg.top_k, cfg.d_ff,
                    cfg.d_ff_shared, cfg.gate, cfg.dtype, getattr(cfg, "capacity", 0),
                    getattr(cfg, "group_size", 0), getattr(cfg, "ffn", "silu"),
-                   getattr(cfg, "bias_mode", "logits"), getattr(cfg, "weight_layout", "row_major"))
+                   getattr(cfg, "bias_mode", "logits"), getattr(cfg, "weight_layout", "row_major"),
+                   getattr(cfg, "router_layout", "row_major"))
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -56,7 +59,14 @@ class Layer:
         return MoeLayer(self.d_model, self.n_routed, self.n_shared, self.top_k, self.d_ff,
                         self.d_ff_shared, _GATE[self.gate], _DT[self.dtype][0], self.capacity,
                         self.group_size, _FFN[self.ffn], _BIAS[self.bias_mode],
-                        _LAYOUT[self.weight_layout])
+                        _LAYOUT[self.weight_layout], _RLAYOUT[self.router_layout])
+
+    @property
+    def router_shape(self) -> tuple:
+        """Shape of w_router: [N_r, d], or [MOE_ROUTER_PAD_ROWS(N_r), d] packed."""
+        if self.router_layout == "packed":
+            return (_lib.router_pad_rows(self.n_routed), self.d_model)
+        return (self.n_routed, self.d_model)
 
 
 def _p(t):
@@ -96,7 +106,7 @@ def route(layer: Layer, x, w_router, bias=None):
     T = x.shape[0]
     dt = layer.torch_dtype
     _check(x, (T, layer.d_model), dt, "x")
-    _check(w_router, (layer.n_routed, layer.d_model), torch.float32, "w_router", x.device)
+    _check(w_router, layer.router_shape, torch.float32, "w_router", x.device)
     _check(bias, (layer.n_routed,), torch.float32, "bias", x.device)
     idx = torch.empty((T, layer.top_k), dtype=torch.int32, device=x.device)
     w = torch.empty((T, layer.top_k), dtype=torch.float32, device=x.device)
@@ -119,6 +129,15 @@ def route_noisy(layer: Layer, x, w_router, bias, w_noise, noise):
     call("moe_route_noisy", ctypes.byref(layer.c()), T, _p(x), _p(w_router), _p(bias), _p(w_noise),
          _p(noise), _p(idx), _p(w), _stream())
     return idx, w
+
+
+def pack_router(layer: Layer, w_router):
+    """w_router [N_r, d] fp32 in the packed router order: [MOE_ROUTER_PAD_ROWS(N_r), d]."""
+    _check(w_router, (layer.n_routed, layer.d_model), torch.float32, "w_router")
+    out = torch.empty((_lib.router_pad_rows(layer.n_routed), layer.d_model), dtype=torch.float32,
+                      device=w_router.device)
+    call("moe_pack_router", ctypes.byref(layer.c()), _p(w_router), _p(out), _stream())
+    return out
 
 
 def pack_weights(layer: Layer, w):
@@ -151,7 +170,7 @@ def route_stats(layer: Layer, x, w_router, bias=None, n_devices: int = 1, lse: b
     T = x.shape[0]
     dt = layer.torch_dtype
     _check(x, (T, layer.d_model), dt, "x")
-    _check(w_router, (layer.n_routed, layer.d_model), torch.float32, "w_router", x.device)
+    _check(w_router, layer.router_shape, torch.float32, "w_router", x.device)
     _check(bias, (layer.n_routed,), torch.float32, "bias", x.device)
     idx = torch.empty((T, layer.top_k), dtype=torch.int32, device=x.device)
     w = torch.empty((T, layer.top_k), dtype=torch.float32, device=x.device)
@@ -253,7 +272,7 @@ class Forward:
         L, dt, dev = self.layer, self.layer.torch_dtype, self.device
         d, N, I, Ks, Is = L.d_model, L.n_routed, L.d_ff, L.n_shared, L.d_ff_shared
         _check(x, (self.T, d), dt, "x", dev)
-        _check(w_router, (N, d), torch.float32, "w_router", dev)
+        _check(w_router, self.layer.router_shape, torch.float32, "w_router", dev)
         _check(bias, (N,), torch.float32, "bias", dev)
         _check(w_gate, (N, I, d), dt, "w_gate", dev)
         _check(w_up, (N, I, d), dt, "w_up", dev)

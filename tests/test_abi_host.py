@@ -23,7 +23,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     L = _lib.lib()
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib.EXPORTS)
@@ -43,7 +43,7 @@ def test_checked_library_exports_the_same_functions():
 
 def test_version_and_status_strings():
     L = _lib.lib()
-    assert L.moe_abi_version() == 3
+    assert L.moe_abi_version() == 4
     assert _lib.status_str(MOE_OK) == "ok"
     assert "workspace" in _lib.status_str(MOE_ERR_WORKSPACE_TOO_SMALL)
     assert L.moe_last_hip_error() == 0
@@ -99,6 +99,12 @@ def test_workspace_size_scales_with_tokens():
     (dict(weight_layout=1, d_model=2000), 8, MOE_ERR_UNSUPPORTED),
     (dict(weight_layout=1, dtype=MOE_F32), 8, MOE_ERR_UNSUPPORTED),
     (dict(weight_layout=5), 8, MOE_ERR_INVALID_ARG),
+    (dict(router_layout=1), 8, MOE_OK),                            # bf16, d % 64, N_r <= 128
+    (dict(router_layout=1, n_routed=128), 8, MOE_OK),
+    (dict(router_layout=1, n_routed=129), 8, MOE_ERR_UNSUPPORTED),  # past the matrix-core router
+    (dict(router_layout=1, d_model=2000), 8, MOE_ERR_UNSUPPORTED),
+    (dict(router_layout=1, dtype=MOE_F32), 8, MOE_ERR_UNSUPPORTED),
+    (dict(router_layout=2), 8, MOE_ERR_INVALID_ARG),
 ])
 def test_layer_validation(kw, T, want):
     st, _ = ws_size(layer(**kw), T)
@@ -147,6 +153,29 @@ def test_pack_weights_argument_errors():
     assert L.moe_pack_weights(ctypes.byref(f32), 2, 128, 64, a, b, None) == MOE_ERR_UNSUPPORTED
     assert L.moe_pack_weights(ctypes.byref(lay), 0, 128, 64, a, b, None) == MOE_OK   # nothing to do
     assert L.moe_pack_weights(ctypes.byref(lay), 0, 128, 64, None, None, None) == MOE_OK
+
+
+def test_pack_router_argument_errors():
+    L = _lib.lib()
+    lay = layer()                                   # N_r = 64, d = 2048: 64 x 2048 floats
+    P = ctypes.c_void_p
+    a = FAKE
+    n = 64 * 2048 * 4                               # bytes of src and of dst
+    # every call below fails its checks, so nothing is launched
+    assert L.moe_pack_router(ctypes.byref(lay), P(a), P(a), None) == MOE_ERR_INVALID_ARG
+    assert L.moe_pack_router(ctypes.byref(lay), P(a), P(a + n - 16), None) == MOE_ERR_INVALID_ARG
+    assert L.moe_pack_router(ctypes.byref(lay), P(a + n - 16), P(a), None) == MOE_ERR_INVALID_ARG
+    assert L.moe_pack_router(ctypes.byref(lay), None, P(a), None) == MOE_ERR_INVALID_ARG
+    assert L.moe_pack_router(ctypes.byref(lay), P(a), None, None) == MOE_ERR_INVALID_ARG
+    assert L.moe_pack_router(ctypes.byref(lay), P(a), P(a + n + 2), None) == MOE_ERR_UNSUPPORTED
+    for kw in (dict(dtype=MOE_F32), dict(d_model=2000), dict(n_routed=129, top_k=6)):
+        assert L.moe_pack_router(ctypes.byref(layer(**kw)), P(a), P(a + (1 << 30)), None) == \
+            MOE_ERR_UNSUPPORTED
+    # moe_route_noisy reads row-major W_g only
+    packed = layer(router_layout=1)
+    f = P(FAKE)
+    assert L.moe_route_noisy(ctypes.byref(packed), 16, f, f, None, f, f, f, f, None) == \
+        MOE_ERR_UNSUPPORTED
 
 
 def test_route_stats_argument_errors():
