@@ -57,6 +57,18 @@ __device__ __forceinline__ float row_ror(float v) {
   return __int_as_float(row_ror<O>(__float_as_int(v)));
 }
 
+// DPP lane permutations inside groups of 8: the mirror of the half row
+// (lane i <- lane 7 - i) and the quad swaps (i <- i ^ 2, i <- i ^ 1).
+template <int CTRL>
+__device__ __forceinline__ int dpp_perm(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_perm(float v) {
+  return __int_as_float(dpp_perm<CTRL>(__float_as_int(v)));
+}
+constexpr int kDppHalfMirror = 0x141, kDppQuadXor2 = 0x4E, kDppQuadXor1 = 0xB1;
+
 // Reductions over aligned groups of W lanes (W a power of two <= 64): a
 // butterfly over the offsets W/2, ..., 2, 1, each lane combining its value
 // with that of lane i ^ o.  Groups of 16 (a DPP row) take the partner by a
@@ -64,10 +76,18 @@ __device__ __forceinline__ float row_ror(float v) {
 // already holds the same value as the lanes i ^ 2o, i ^ 4o, ..., so lane
 // i + o (mod 16), whichever way the row turns, holds the value of lane
 // i ^ o.  The combined operands, and so the results, are those of the xor
-// shuffles bit for bit.
+// shuffles bit for bit.  Groups of 8 (half a DPP row) first combine lane i
+// with lane 7 - i, then take the quad swaps i ^ 2 and i ^ 1: after the
+// first step lanes i and 7 - i hold the same pair, so every lane ends with
+// the same two partial results combined (in one order or the other), and
+// max, min and sum come out bit-identical on all 8 lanes.
 template <int W>
 __device__ __forceinline__ float group_max(float v) {
-  if constexpr (W == 16) {
+  if constexpr (W == 8) {
+    v = fmaxf(v, dpp_perm<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_perm<kDppQuadXor2>(v));
+    return fmaxf(v, dpp_perm<kDppQuadXor1>(v));
+  } else if constexpr (W == 16) {
     v = fmaxf(v, row_ror<8>(v));
     v = fmaxf(v, row_ror<4>(v));
     v = fmaxf(v, row_ror<2>(v));
@@ -80,7 +100,11 @@ __device__ __forceinline__ float group_max(float v) {
 }
 template <int W>
 __device__ __forceinline__ float group_sum(float v) {
-  if constexpr (W == 16) {
+  if constexpr (W == 8) {
+    v += dpp_perm<kDppHalfMirror>(v);
+    v += dpp_perm<kDppQuadXor2>(v);
+    return v + dpp_perm<kDppQuadXor1>(v);
+  } else if constexpr (W == 16) {
     v += row_ror<8>(v);
     v += row_ror<4>(v);
     v += row_ror<2>(v);
@@ -93,7 +117,11 @@ __device__ __forceinline__ float group_sum(float v) {
 }
 template <int W>
 __device__ __forceinline__ int group_min_int(int v) {
-  if constexpr (W == 16) {
+  if constexpr (W == 8) {
+    v = min(v, dpp_perm<kDppHalfMirror>(v));
+    v = min(v, dpp_perm<kDppQuadXor2>(v));
+    return min(v, dpp_perm<kDppQuadXor1>(v));
+  } else if constexpr (W == 16) {
     v = min(v, row_ror<8>(v));
     v = min(v, row_ror<4>(v));
     v = min(v, row_ror<2>(v));

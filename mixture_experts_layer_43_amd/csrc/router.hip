@@ -83,25 +83,38 @@ __device__ __forceinline__ void select_and_store(const float (&z)[EPL], const fl
                                                  float* __restrict__ topk_w,
                                                  StatAcc<EPL>* sa = nullptr,
                                                  float* __restrict__ lse = nullptr) {
+  // zs: the logits still in the running, NaN for experts past N_r and for
+  // the chosen ones (fmaxf skips NaN and NaN equals nothing).  A lane's
+  // experts ascend with q, so its first q whose logit equals the group
+  // maximum is its lowest candidate id.  The chosen id c lives on lane
+  // c % NP as q = c / NP.
   bool sel[EPL];
+  float zs[EPL];
 #pragma unroll
-  for (int q = 0; q < EPL; ++q) sel[q] = false;
+  for (int q = 0; q < EPL; ++q) {
+    sel[q] = false;
+    zs[q] = ev[q] ? z[q] : __builtin_nanf("");
+  }
+  const int gl = lane % NP;
   float zmax = -INFINITY;
   for (int r = 0; r < K; ++r) {
     float m = -INFINITY;
 #pragma unroll
-    for (int q = 0; q < EPL; ++q)
-      if (!sel[q]) m = fmaxf(m, z[q]);
+    for (int q = 0; q < EPL; ++q) m = fmaxf(m, zs[q]);
     m = group_max<NP>(m);
     if (r == 0) zmax = m;
     int cand = 0x7FFFFFFF;
 #pragma unroll
-    for (int q = 0; q < EPL; ++q)
-      if (!sel[q] && ev[q] && z[q] == m) cand = min(cand, e[q]);
+    for (int q = EPL - 1; q >= 0; --q) cand = zs[q] == m ? e[q] : cand;
     cand = group_min_int<NP>(cand);
+    const int qc = (cand & (NP - 1)) == gl ? static_cast<int>(static_cast<unsigned>(cand) / NP) : -1;
 #pragma unroll
-    for (int q = 0; q < EPL; ++q)
-      if (e[q] == cand) sel[q] = true;
+    for (int q = 0; q < EPL; ++q) {
+      if (q == qc) {
+        sel[q] = true;
+        zs[q] = __builtin_nanf("");
+      }
+    }
   }
   if (bias_sel) {
     // Gates from the unbiased logits: the largest over all experts (gate 0)
@@ -548,7 +561,8 @@ __device__ __forceinline__ void router_stream(f32x16 (&acc)[MBLK][NBLK], __amdgp
 // stream W_g through a ring of RD slices.  Each W_g value is split once for
 // all MBLK token blocks.  The partial logit tiles are summed in
 // LDS in wavefront order (deterministic), then each wavefront selects for
-// four tokens at a time.  PK: W_g in the packed order of moe_pack_router.
+// its TB / kRW tokens in one pass.  PK: W_g in the packed order of
+// moe_pack_router.
 //
 // Small batches split K over KS workgroups per token block as well
 // (blockIdx.y); each then writes its summed tile to partial[ks][t][e] and
@@ -562,16 +576,16 @@ __global__ __launch_bounds__(kRW * kWave) void router_mfma_kernel(
     const float* __restrict__ eps) {
   constexpr int TB = 32 * MBLK;
   constexpr int NPAD = 32 * NBLK;
-  // Selection: groups of 16 lanes, one token each (4-step reductions).
-  constexpr int NP = 16;
+  // Selection: one token per group of NP lanes, so that the workgroup's
+  // kRW * 64 lanes take all TB tokens in one pass (16 lanes for 32 tokens,
+  // 8 for 64; DPP reductions of 4 or 3 steps).
+  constexpr int NP = kRW * kWave / TB;
   constexpr int EPL = NPAD / NP;
   constexpr int G = kWave / NP;
+  static_assert(NP == 8 || NP == 16, "selection groups");
   constexpr int RS = 16 / MBLK;               // x slices per round
   constexpr int RD = (MBLK * NBLK <= 2) ? 4 : 2;  // W_g slices in flight
   static_assert((TB / kRW) % G == 0, "token split");
-  __shared__ __align__(16) float lg[TB][NPAD + 1];
-  static_assert(!STATS || sizeof(lg) >= kRW * (2 * NPAD + 1) * sizeof(double),
-                "statistics reduction reuses the logit tile");
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -611,9 +625,15 @@ __global__ __launch_bounds__(kRW * kWave) void router_mfma_kernel(
 
   // One LDS slot per wavefront: its x ring while it streams, then its
   // partial logit tile (the ring is idle by then and private to the
-  // wavefront, so no barrier separates the two uses).
-  constexpr int SLOTF = TB * (NPAD > 64 ? NPAD : 64);
-  static_assert(SLOTF >= TB * NPAD && SLOTF * 4 >= 2 * TB * 128, "LDS slot");
+  // wavefront, so no barrier separates the two uses).  The tile is stored
+  // column-major, logit (t, e) at e*LDT + t: a lane's accumulator holds four
+  // consecutive tokens of one expert, one 16-byte write, and the padding of
+  // LDT keeps 16 consecutive experts on distinct banks.
+  constexpr int LDT = TB + 4;
+  constexpr int SLOTF = NPAD * LDT > 64 * TB ? NPAD * LDT : 64 * TB;
+  static_assert(SLOTF * 4 >= 2 * TB * 128, "x ring");
+  static_assert(!STATS || (kRW - 1) * SLOTF * 4 >= kRW * (2 * NPAD + 1) * 8,
+                "statistics reduction reuses slots 1..");
   __shared__ __align__(16) float slot[kRW][SLOTF];
 
   const int S = d / 16;
@@ -651,32 +671,45 @@ __global__ __launch_bounds__(kRW * kWave) void router_mfma_kernel(
   if (rs + 1 <= s1) router_round<1, RD, MBLK, NBLK, PK>(acc, xp, wp, rs);
 
   // Sum of the wavefronts' partial tiles in wavefront order: each writes its
-  // tile to its own LDS slot, then every thread adds its elements' kRW
-  // values in order (the same additions as accumulating wave by wave).
+  // tile to its own LDS slot, then every thread adds the kRW values of its
+  // elements in order (the same additions as accumulating wave by wave),
+  // up to four tokens of one expert at a time, into slot 0 in place (no
+  // other thread reads those elements).
   // D[row][col] of a 32x32 block: lane (col + 32*h), register v, row 8*(v/4) + 4*h + v%4.
 #pragma unroll
   for (int mb = 0; mb < MBLK; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NBLK; ++nb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        slot[wave][r * NPAD + nb * 32 + lr] = acc[mb][nb][v];
+      for (int j = 0; j < 4; ++j) {
+        const int r0 = mb * 32 + 8 * j + 4 * (lane >> 5);
+        const f32x4 v = {acc[mb][nb][4 * j], acc[mb][nb][4 * j + 1], acc[mb][nb][4 * j + 2],
+                         acc[mb][nb][4 * j + 3]};
+        *reinterpret_cast<f32x4*>(&slot[wave][(nb * 32 + lr) * LDT + r0]) = v;
       }
   __syncthreads();
-  for (int i = threadIdx.x; i < TB * NPAD; i += kRW * kWave) {
-    float sum = slot[0][i];
+  // VW consecutive tokens per thread and step: 4 where the tile gives every
+  // thread at least that many elements, else fewer, so all threads work.
+  constexpr int VW = TB * NPAD >= 4 * kRW * kWave ? 4 : TB * NPAD >= 2 * kRW * kWave ? 2 : 1;
+  typedef float fvw __attribute__((ext_vector_type(VW)));
+  for (int g = threadIdx.x; g < NPAD * (TB / VW); g += kRW * kWave) {
+    const int off = (g / (TB / VW)) * LDT + (g % (TB / VW)) * VW;
+    fvw v[kRW];
 #pragma unroll
-    for (int w = 1; w < kRW; ++w) sum += slot[w][i];
-    lg[i / NPAD][i % NPAD] = sum;
+    for (int w = 0; w < kRW; ++w) v[w] = *reinterpret_cast<const fvw*>(&slot[w][off]);
+    fvw sum = v[0];
+#pragma unroll
+    for (int w = 1; w < kRW; ++w) sum += v[w];
+    *reinterpret_cast<fvw*>(&slot[0][off]) = sum;
   }
   __syncthreads();
+  const float* lgt = &slot[0][0];   // logit (t, e) at e*LDT + t
 
   if (KS > 1) {
     for (int i = threadIdx.x; i < TB * NPAD; i += kRW * kWave) {
       const int tl = i / NPAD, c = i % NPAD;
       const int64_t t = tok0 + tl;
-      if (t < T) partial[(static_cast<int64_t>(blockIdx.y) * T + t) * NPAD + c] = lg[tl][c];
+      if (t < T) partial[(static_cast<int64_t>(blockIdx.y) * T + t) * NPAD + c] = lgt[c * LDT + tl];
     }
     return;
   }
@@ -703,9 +736,9 @@ __global__ __launch_bounds__(kRW * kWave) void router_mfma_kernel(
       // Read first, then select values (e[q] < NPAD, inside the tile): a
       // select between two loads would become a load through a selected
       // pointer and push z to scratch.
-      float v = lg[tl][e[q]];
+      float v = lgt[e[q] * LDT + tl];
       if (wn != nullptr) {   // noisy gating: + eps * softplus(x . wn_e), row N_r + e
-        const float nv = lg[tl][min(Nr + e[q], NPAD - 1)];
+        const float nv = lgt[min(Nr + e[q], NPAD - 1) * LDT + tl];
         v = fmaf(eps[t * Nr + min(e[q], Nr - 1)], softplus_f32(nv), v);
       }
       z[q] = evq[q] ? v + bq[q] : -INFINITY;
@@ -715,7 +748,7 @@ __global__ __launch_bounds__(kRW * kWave) void router_mfma_kernel(
                                      topk_w, &sa, lse);
   }
   if constexpr (STATS)
-    block_stats<NP, EPL, kRW>(sa, lane, wave, reinterpret_cast<double*>(&lg[0][0]),
+    block_stats<NP, EPL, kRW>(sa, lane, wave, reinterpret_cast<double*>(&slot[1][0]),
                               stats_part + static_cast<int64_t>(blockIdx.x) * kStatsStride);
 }
 
