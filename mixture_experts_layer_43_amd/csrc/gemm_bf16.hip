@@ -618,12 +618,21 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
     // at compile time, which the LDS store takes as its immediate.
     static_assert(TM % 8 == 0, "wavefront rows start at multiples of 8");
     char* const cl = reinterpret_cast<char*>(smem) + (wm * TM + hrow) * (OUT_N * 2);
-    int colb[NBO][4];
+    // Each LDS write is a whole dword: lanes c and c ^ 1 (adjacent columns,
+    // the same rows) swap halves of their converted row pairs (one DPP quad
+    // exchange), so the even-column lane holds row r of columns c, c + 1
+    // and the odd one row r + 1 of columns c - 1, c.  dcol: the byte offset
+    // of that dword for register pair u = 0, 2 (the odd lane's row is one
+    // further down).
+    const int odd = col_in & 1;
+    const uint32_t psel = odd ? 0x03020706u : 0x05040100u;
+    int dcol[NBO][2];
 #pragma unroll
     for (int j = 0; j < NBO; ++j) {
-      const int c = wn * TNO + j * 32 + col_in;
+      const int c = (wn * TNO + j * 32 + col_in) & ~1;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) colb[j][u] = ((((c >> 3) ^ (hrow + u)) << 3) + (c & 7)) * 2;
+      for (int u = 0; u < 2; ++u)
+        dcol[j][u] = ((((c >> 3) ^ (hrow + 2 * u + odd)) << 3) + (c & 7)) * 2 + odd * (OUT_N * 2);
     }
     auto stage = [&](auto relu) {
 #pragma unroll
@@ -643,11 +652,14 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
               e0 = acc[i][j][v];
               e1 = acc[i][j][v + 1];
             }
+            // pr: rows r, r + 1 of this lane's column; pq: the same of the
+            // neighbour column.
             const uint32_t pr = pack_bf16x2(e0, e1);
+            const uint32_t pq = static_cast<uint32_t>(
+                __builtin_amdgcn_update_dpp(0, static_cast<int>(pr), 0xB1, 0xF, 0xF, false));
             const int ro = (i * 32 + 8 * (v >> 2) + (v & 3)) * (OUT_N * 2);
-            *reinterpret_cast<bf16_t*>(cl + ro + colb[j][v & 3]) = static_cast<bf16_t>(pr);
-            *reinterpret_cast<bf16_t*>(cl + ro + OUT_N * 2 + colb[j][(v & 3) + 1]) =
-                static_cast<bf16_t>(pr >> 16);
+            *reinterpret_cast<uint32_t*>(cl + ro + dcol[j][(v & 3) >> 1]) =
+                __builtin_amdgcn_perm(pq, pr, psel);
           }
     };
     if (MODE == kDown && p.relu)
