@@ -5,6 +5,8 @@ forward is within the layer rules of the oracle.  Every call goes through the
 C ABI; PyTorch only supplies the graph object and the capture stream."""
 from __future__ import annotations
 
+import dataclasses
+
 import pytest
 import torch
 
@@ -16,15 +18,24 @@ from test_gpu_parity import announce, cfg_of
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name,noalloc", [("16b-decode", False), ("16b-decode", True),
-                                          ("mid-ragged", False), ("mid-ragged", True),
-                                          ("mid-f32", False)])
-def test_graph_replays_equal_the_eager_forward(name, noalloc):
+@pytest.mark.parametrize("name,noalloc,packed", [("16b-decode", False, False), ("16b-decode", True, False),
+                                                 ("16b-decode", False, True),
+                                                 ("mid-ragged", False, False), ("mid-ragged", True, False),
+                                                 ("mid-f32", False, False)])
+def test_graph_replays_equal_the_eager_forward(name, noalloc, packed):
+    """packed: expert weights and W_g in their packed orders, as bench.py
+    captures the decode-shaped forward."""
     cfg = cfg_of(name)
-    announce(f"graph capture {name} noalloc={noalloc}")
+    announce(f"graph capture {name} noalloc={noalloc} packed={packed}")
     inp = prepare(cfg)
     d = upload(inp)
-    f = ops.Forward(ops.Layer.of(cfg), cfg.tokens, torch.device("cuda"), noalloc=noalloc)
+    lay = ops.Layer.of(cfg)
+    if packed:
+        for k in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down"):
+            d[k] = ops.pack_weights(lay, d[k])
+        d["w_router"] = ops.pack_router(lay, d["w_router"])
+        lay = dataclasses.replace(lay, weight_layout="packed", router_layout="packed")
+    f = ops.Forward(lay, cfg.tokens, torch.device("cuda"), noalloc=noalloc)
     args = [d[k] for k in ("x", "w_router", "bias", "w_gate", "w_up", "w_down", "ws_gate", "ws_up",
                            "ws_down")]
     f(*args)
