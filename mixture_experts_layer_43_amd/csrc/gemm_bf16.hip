@@ -602,18 +602,22 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
     // free now) so that the global stores are whole 16-byte chunks of rows,
     // a row of the tile per 16..32 lanes; they are non-temporal (the tile
     // is not read again by this kernel).  In LDS, 16-byte chunk k of tile
-    // row r sits at chunk k ^ (r & 7), so both the 2-byte writes and the
-    // 16-byte reads spread over the banks.
+    // row r sits at chunk k ^ csw(r), csw(r) = (r & 7) ^ 4 (r & 1).  The LDS
+    // takes a dword write in two halves of 32 lanes over 32 banks; the half
+    // that writes rows r and r + 1 (r even) of a wavefront's 32 columns then
+    // finds them in the two different halves of the 32 banks (with
+    // csw(r) = r & 7 they shared them, two ways), and the 16-byte reads of
+    // eight consecutive chunks of a row still cover all banks.
     constexpr int NT = WM * WN * kWave;
     static_assert(OUT_N % 64 == 0 && BM * OUT_N <= STAGES * SE, "C tile does not fit the stages");
     __syncthreads();  // every wavefront is done reading the last stage
     bf16_t* ct = smem;
-    auto cpos = [](int r, int c) { return r * OUT_N + ((((c >> 3) ^ (r & 7))) << 3) + (c & 7); };
+    auto csw = [](int r) { return (r & 7) ^ ((r & 1) << 2); };
+    auto cpos = [&](int r, int c) { return r * OUT_N + ((((c >> 3) ^ csw(r))) << 3) + (c & 7); };
     const int col_in = lane & 31;
     // Rows r and r + 1 of a column (registers v, v + 1 for even v) are
-    // converted together and written as the two halves of one dword.  The
-    // byte address of an element is a lane part per (j, v % 4) - the
-    // swizzle sees only the row's low three bits, hrow + v % 4, as every
+    // converted together.  The byte address of a write is a lane part per
+    // (j, v % 4) - the swizzle sees only the row's low three bits, as every
     // wavefront's rows start at a multiple of 8 - plus a row offset known
     // at compile time, which the LDS store takes as its immediate.
     static_assert(TM % 8 == 0, "wavefront rows start at multiples of 8");
@@ -632,7 +636,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void grouped_gemm_bf16(GemmArgs p)
       const int c = (wn * TNO + j * 32 + col_in) & ~1;
 #pragma unroll
       for (int u = 0; u < 2; ++u)
-        dcol[j][u] = ((((c >> 3) ^ (hrow + 2 * u + odd)) << 3) + (c & 7)) * 2 + odd * (OUT_N * 2);
+        dcol[j][u] = ((((c >> 3) ^ csw(hrow + 2 * u + odd)) << 3) + (c & 7)) * 2 + odd * (OUT_N * 2);
     }
     auto stage = [&](auto relu) {
 #pragma unroll
