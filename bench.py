@@ -71,8 +71,8 @@ DECODE_STEPS_MULT = 10
 GEMM_SOURCE = os.path.join(ROOT, "mixture_experts_layer_43_amd", "csrc", "gemm_bf16.hip")
 TRAFFIC_BYTES = {
     # profiles/moe_layer_16b_counters.md, profiles/moe_layer_16b-decode_counters.md
-    ("16b", "packed"): {"bytes": 4061807872, "gemm_sha": "0e1361ebf1810e9a"},
-    ("16b-decode", "packed"): {"bytes": 769561088, "gemm_sha": "0e1361ebf1810e9a"},
+    ("16b", "packed"): {"bytes": 4065112789, "gemm_sha": "4c511375cb5efa38"},
+    ("16b-decode", "packed"): {"bytes": 768868651, "gemm_sha": "4c511375cb5efa38"},
 }
 
 
