@@ -7,14 +7,20 @@ routed width or another one; 1..3000 tokens; both gates, the SiLU and ReLU
 FFNs, both bias modes and sometimes an expert capacity.  Routing and counts
 must match bit for bit and y within the layer's tolerance (tests/_parity.py),
 as for the hand-picked shapes.  Sizes stay small enough for the oracle to
-finish each case in well under a second."""
+finish each case in well under a second.  Where the layer admits the packed
+router order (bf16, d % 64 == 0, N_r <= 128) the forward on packed W_g must
+also equal the row-major one bit for bit."""
 from __future__ import annotations
+
+import dataclasses
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 from _parity import check_gates, check_y, host, prepare, upload
+from mixture_experts_layer_43_amd import ops
 from synth import LayerConfig
 from test_gpu_parity import announce, run_forward
 
@@ -58,9 +64,20 @@ def test_random_layer_matches_oracle(i):
              f"{cfg.ffn} bias={cfg.bias_mode} C={cfg.capacity} S={cfg.group_size}")
     inp = prepare(cfg)
     ref = oracle.forward(cfg, inp)
-    f = run_forward(cfg, upload(inp))
+    d = upload(inp)
+    f = run_forward(cfg, d)
     np.testing.assert_array_equal(host(f.topk_idx), ref["topk_idx"])
     np.testing.assert_array_equal(host(f.counts), ref["counts"])
     np.testing.assert_array_equal(host(f.offsets), ref["offsets"])
     check_gates(host(f.topk_w), ref["topk_w"])
     check_y(host(f.y), ref["y"], cfg.dtype)
+    if cfg.dtype == "bf16" and cfg.d_model % 64 == 0 and cfg.n_routed <= 128:
+        lay = ops.Layer.of(cfg)
+        wp = ops.pack_router(lay, d["w_router"])
+        fp = ops.Forward(dataclasses.replace(lay, router_layout="packed"), cfg.tokens, torch.device("cuda"))
+        fp(d["x"], wp, d["bias"], d["w_gate"], d["w_up"], d["w_down"], d.get("ws_gate"), d.get("ws_up"),
+           d.get("ws_down"))
+        torch.cuda.synchronize()
+        assert torch.equal(fp.topk_idx, f.topk_idx)
+        assert torch.equal(fp.topk_w, f.topk_w)
+        assert torch.equal(fp.y, f.y)
