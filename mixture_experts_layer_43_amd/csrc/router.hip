@@ -638,7 +638,13 @@ __global__ __launch_bounds__(kRW * kWave) void router_mfma_kernel(
 
   const int S = d / 16;
   const int range = blockIdx.y * kRW + wave, nranges = KS * kRW;
-  const int s0 = range * S / nranges, s1 = (range + 1) * S / nranges;
+  // Ranges of whole blocks of four slices where every range gets at least
+  // two of them (all stream; e.g. d = 1280: 8 or 12 slices per wavefront
+  // instead of 10), else equal shares of slices.
+  const int NBK = S / 4;
+  const bool by_block = NBK >= 2 * nranges;
+  const int s0 = by_block ? 4 * (range * NBK / nranges) : range * S / nranges;
+  const int s1 = by_block ? 4 * ((range + 1) * NBK / nranges) : (range + 1) * S / nranges;
   // Full rounds of RS slices, then the remainder in rounds of 8, 4, 2, 1.
   int rs = s0;
   // Ranges of two or more whole blocks of four slices stream; the rest (and
