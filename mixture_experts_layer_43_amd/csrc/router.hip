@@ -553,8 +553,10 @@ __device__ __forceinline__ void router_stream(f32x16 (&acc)[MBLK][NBLK], __amdgp
 }
 
 // One workgroup: 32*MBLK tokens x 32*NBLK experts, kRW wavefronts.  The
-// d/16 K slices are cut into kRW contiguous ranges, one per wavefront.  A
-// range of at least two whole blocks of four slices streams (router_stream:
+// d/16 K slices are cut into contiguous ranges, one per wavefront (kRW per
+// workgroup, KS*kRW with split K), at block boundaries of four slices
+// where each range gets two blocks or more.  A range of at least two whole
+// blocks streams (router_stream:
 // x through an LDS ring, W_g - which every workgroup reads, so it stays in
 // L2 - into registers four slices ahead); other ranges load the x
 // fragments of up to RS slices at once (one trip to HBM per round) and
